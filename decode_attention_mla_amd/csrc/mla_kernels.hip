@@ -1,0 +1,845 @@
+// MLA decode attention for MI355X (gfx950): split kernel + combine kernel.
+//
+// What is computed ("FlashMLA-ETAP", gist.science technical summary,
+// Methodology): S = Q K^T, P = softmax(S), O = P V over the shared latent
+// KV rows (576 bf16 channels; V = the first 512).  The pages' design is for
+// Hopper WGMMA, whose M >= 64 forces 16 heads to be padded (Problem
+// Statement); their fix puts the KV length in the M slot (the transposed
+// order S^T = K Q^T).  On CDNA4 the 16x16xK MFMA shapes take 16 heads with
+// no padding, so the slot choice is free; this kernel still puts keys in M
+// for QK^T, because then the score accumulator of a lane (one head, four
+// keys) is exactly the B operand layout that the PV MFMA wants for P^T:
+// P never leaves registers.
+//
+// Work decomposition (one workgroup = 4 waves of 64 lanes):
+//   * A "row block" is 16 query rows: the 16 heads h0..h0+15 of one token.
+//   * Workgroup (g, y) owns key range g of the split plan (plan.h) and row
+//     blocks 4y .. 4y+3.  With fewer than 4 row blocks the spare waves split
+//     the keys: wave w takes row block w % nrb and every nkg-th 16-key block.
+//   * Each wave is an independent flash-decoding worker: its own running
+//     max / sum / O accumulator, no barrier inside the key loop.  The waves
+//     of a segment are merged through LDS at the end, and the result is
+//     either the final output or a partial for the combine kernel.
+//
+// Per 16-key block, per wave:
+//   1. 18 x 16-byte loads per lane bring the 16 latent rows (1152 B each)
+//      straight into MFMA A-operand layout: lane l holds key l%16, channels
+//      32s + 8(l/16) .. +7.  The next block's loads are in flight while the
+//      current one is computed (register double buffer).
+//   2. S^T (16 keys x 16 heads) = 18 MFMA 16x16x32 bf16, fp32 accumulate.
+//   3. The 512 value channels are written to a wave-private LDS tile
+//      (XOR-swizzled 16-byte chunks) for the transposed read PV needs.
+//   4. Online softmax in fp32 (log2 domain); row max over keys = in-lane max
+//      of 4 + two cross-lane xor shuffles; the O rescale is skipped when no
+//      head's max moved.
+//   5. O^T (512 ch x 16 heads) += V^T P^T with 32 + 32 MFMA 16x16x16 bf16:
+//      P is split into bf16 hi + lo parts so that rounding P costs no
+//      accuracy (bf16 P alone gives O errors near 1e-4 at short contexts).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+
+#include "mla_decode.h"
+#include "plan.h"
+
+namespace mla {
+
+constexpr int kDqk = MLA_HEAD_DIM_QK;          // 576
+constexpr int kDv = MLA_HEAD_DIM_V;            // 512
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQkSteps = kDqk / 32;            // 18 MFMA k-steps of 32 channels
+constexpr int kVSteps = kDv / 32;              // the first 16 of them are values
+constexpr int kOutTiles = kDv / 16;            // 32 output tiles of 16 channels
+constexpr int kBlockBytes = kKeyBlock * kDqk * 2;         // 18 KB: one 16-key block
+constexpr int kStages = 2;                                 // LDS ring depth per wave
+constexpr int kRingBytes = kWaves * kStages * kBlockBytes; // 144 KB
+constexpr int kMergePitch = kDv + 4;           // floats per merge row (bank spread)
+constexpr int kMergeFloats = kWaves * 16 * kMergePitch;
+constexpr int kStatFloats = kWaves * 16 * 2;   // running max and sum per wave/head
+constexpr int kLdsBytes = (kMergeFloats + kStatFloats) * 4 > kRingBytes
+                              ? (kMergeFloats + kStatFloats) * 4
+                              : kRingBytes;
+constexpr int kCombineChannels = 64;           // channels per combine workgroup
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+struct Params {
+    const uint16_t *q;
+    const uint16_t *kv;
+    const int32_t *block_table;
+    const int32_t *seqlens;
+    float *out;
+    float *lse;
+    float *part_o;     // [2*splits][n_rb][16][512]
+    float *part_lse;   // [2*splits][n_rb][16], log2 domain
+    int64_t kv_capacity;
+    int64_t num_pages;
+    int64_t capacity;  // keys one sequence can hold
+    int64_t min_chunk;
+    int32_t batch;
+    int32_t s_q;
+    int32_t heads;
+    int32_t page_size;
+    int32_t max_pages;
+    int32_t n_rb;      // row blocks: s_q * heads / 16
+    int32_t splits;    // key ranges (gridDim.x of the split kernel when sized blind)
+    float scale_log2;  // scale * log2(e)
+};
+
+// ---------------------------------------------------------------- wave helpers
+
+__device__ inline int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    return v;
+}
+
+__device__ inline int64_t wave_incl_scan_i64(int64_t v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int64_t t = __shfl_up(v, d);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+__device__ inline int32_t seq_len(const Params &p, int b) {
+    return clamp_len(p.seqlens[b], p.capacity);
+}
+
+// Total padded keys over all sequences (every lane gets the sum).
+__device__ inline int64_t plan_total(const Params &p, int lane) {
+    int64_t total = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        total += wave_sum_i64(b < p.batch ? padded_len(seq_len(p, b)) : 0);
+    }
+    return total;
+}
+
+__device__ inline uint16_t bf16_bits(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ inline float bf16_value(uint16_t bits) {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+
+// Wave-local ordering of LDS accesses: the same wave writes a tile and reads
+// it back in another lane order; LDS executes one wave's accesses in order,
+// this keeps the compiler from moving them across each other.
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------- per-wave state
+
+struct WaveState {
+    f32x4 acc[kOutTiles];  // O^T tiles: lane l -> head l%16, channels 16ct + 4(l/16) + i
+    float m;               // running max of the scaled scores (log2 domain)
+    float l;               // this lane's share of the running sum
+};
+
+struct BlockCtx {
+    const uint16_t *kv;
+    const int32_t *table_row;  // block table row of the sequence (paged)
+    int64_t seq_base;          // contiguous: first row of the sequence
+    int32_t page_size;         // 0 = contiguous
+    int64_t num_pages;
+    int32_t last_key;          // L - 1: loads of keys past it are clamped to it
+};
+
+// LDS image of one 16-key block: 18 slices of 1 KB; slice t holds the 16-byte
+// chunks 4t .. 4t+3 (channels 32t .. 32t+31) of the 16 rows, chunk 4t + q of
+// row k at slot 16q + (k ^ 2(q & 1)).  The K operand of QK^T for step t is
+// then one contiguous 1 KB read per wave, and the transposed value reads of
+// PV hit 8 distinct 16-byte bank groups.
+__device__ inline int slot_of(int q, int k) { return 16 * q + (k ^ (2 * (q & 1))); }
+
+// Issue the 18 direct-to-LDS 16-byte loads of the block starting at key kb.
+// Lane l of load t fetches row k = (l & 15) ^ 2((l >> 4) & 1), chunk
+// 4t + (l >> 4), and the hardware stores it at slice t, slot l.
+__device__ inline void issue_block(char *stage, const BlockCtx &c, int kb, int lane) {
+    const int q = lane >> 4;
+    const int k = (lane & 15) ^ (2 * (q & 1));
+    const int key = min(kb + k, c.last_key);
+    const uint16_t *row;
+    if (c.page_size) {
+        int64_t page = c.table_row[kb / c.page_size];  // one page per 16-key block
+        page = page < 0 ? 0 : (page >= c.num_pages ? c.num_pages - 1 : page);
+        row = c.kv + (page * c.page_size + key % c.page_size) * (int64_t)kDqk;
+    } else {
+        row = c.kv + (c.seq_base + key) * (int64_t)kDqk;
+    }
+    row += 8 * q;
+#pragma unroll
+    for (int t = 0; t < kQkSteps; ++t)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(row + 32 * t),
+                                         (__attribute__((address_space(3))) void *)(stage + t * 1024),
+                                         16, 0, 0);
+}
+
+// The compiler does not track completion of direct-to-LDS loads, so the
+// waits are explicit: at most N vector-memory operations may stay in flight.
+// (s_waitcnt through the builtin, so the compiler's own wait insertion sees
+// it; the empty asm statements keep memory accesses from moving across.)
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+}
+
+__device__ inline void wait_lgkm0() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (0x7 << 4));
+    asm volatile("" ::: "memory");
+}
+
+// Scores of one block: S^T[key][head] for 16 keys x 16 heads, scaled into the
+// log2 domain and masked.  Lane l holds head l%16, keys kb + 4(l/16) + i.
+// The A operand (K) comes from the block's LDS image: lane l -> key l%16,
+// channels 32t + 8(l/16) .. +7; the B operand Q^T is in registers.
+__device__ inline void block_scores(float (&sv)[4], float &mx, const char *stage,
+                                    const bf16x8 (&qf)[kQkSteps], int kb, int key_end,
+                                    float scale_log2, int lane) {
+    const int grp = lane >> 4;
+    const char *kop = stage + slot_of(grp, lane & 15) * 16;
+    bf16x8 ka[kQkSteps];  // all K operands first: the reads overlap each other
+#pragma unroll
+    for (int t = 0; t < kQkSteps; ++t) ka[t] = *reinterpret_cast<const bf16x8 *>(kop + t * 1024);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kQkSteps; ++t)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t], qf[t], s, 0, 0, 0);
+    const int k0 = kb + 4 * grp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (k0 + i < key_end) ? s[i] * scale_log2 : -INFINITY;
+    mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// P = exp2(s - m) and O^T += V^T P^T for one block.  P^T is already in the
+// 16x16x16 B layout (lane: head l%16, keys 4(l/16) + i) and is split into
+// bf16 hi + lo parts.  The A operand (V^T: lane l -> channel 16ct + l%16,
+// keys 4(l/16) + i) is read from the block image: channel chunk
+// c = 2ct + (l%16)/8 lives in slice c/4 at slot_of(c%4, key).
+__device__ inline void block_pv(WaveState &st, const float (&sv)[4], const char *stage, int lane) {
+    const int grp = lane >> 4;
+    const int n = lane & 15;
+    s16x4 va[kOutTiles];  // all V^T operands first
+#pragma unroll
+    for (int ct = 0; ct < kOutTiles; ++ct) {
+        const int c = 2 * ct + (n >> 3);
+        const char *base = stage + (c >> 2) * 1024 + ((n & 7) << 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            va[ct][i] = *reinterpret_cast<const short *>(base + slot_of(c & 3, 4 * grp + i) * 16);
+    }
+    s16x4 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(sv[i] - st.m);
+        psum += pr;
+        const uint16_t h = bf16_bits(pr);
+        phi[i] = (short)h;
+        plo[i] = (short)bf16_bits(pr - bf16_value(h));
+    }
+    st.l += psum;
+#pragma unroll
+    for (int ct = 0; ct < kOutTiles; ++ct) {
+        st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], phi, st.acc[ct], 0, 0, 0);
+        st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], plo, st.acc[ct], 0, 0, 0);
+    }
+}
+
+// The running max m is only a reference point: P = exp2(s - m) may exceed 1
+// as long as s - m <= kMaxLag, so the accumulators are rescaled only when a
+// block's max passes m + kMaxLag (and for the first block).  The result is
+// the same softmax; the rescale sits outside the hot loop.
+constexpr float kMaxLag = 8.0f;
+
+// --------------------------------------------------------------- split kernel
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_split_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = blockIdx.x;
+    const int rb0 = blockIdx.y * kWaves;
+    const int nrb = min(kWaves, p.n_rb - rb0);
+    const int nkg = kWaves / nrb;
+    const int my_rbl = wave % nrb;
+    const int my_kg = wave / nrb;
+    const bool active = my_kg < nkg;
+    const int hpt = p.heads >> 4;
+    const int rb = rb0 + my_rbl;
+    const int tok = rb / hpt;
+    const int h0 = (rb % hpt) * 16;
+
+    // Plan (same arithmetic as mla_plan on the host).
+    const int64_t total = plan_total(p, lane);
+    const int64_t chunk = plan_chunk(total, p.splits, p.min_chunk);
+    const int64_t gs = (int64_t)g * chunk;
+    if (gs >= total) return;  // uniform over the workgroup
+    const int64_t ge = min(gs + chunk, total);
+
+    char *ring = lds + wave * kStages * kBlockBytes;
+    float *merge_o = reinterpret_cast<float *>(lds);
+    float *merge_m = merge_o + kMergeFloats;
+    float *merge_l = merge_m + kWaves * 16;
+
+    int64_t base = 0;
+    for (int b0 = 0; b0 < p.batch && base < ge; b0 += 64) {
+        const int bl = b0 + lane;
+        const int32_t Ll = bl < p.batch ? seq_len(p, bl) : 0;
+        const int64_t lpl = padded_len(Ll);
+        const int64_t incl = wave_incl_scan_i64(lpl, lane) + base;
+        const int64_t stl = incl - lpl;
+        uint64_t mask = __ballot(bl < p.batch && lpl > 0 && stl < ge && incl > gs);
+        const int64_t next_base = __shfl(incl, 63);
+
+        while (mask) {
+            const int j = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int b = b0 + j;
+            const int64_t st_b = __shfl(stl, j);
+            const int32_t L = __shfl(Ll, j);
+            const int64_t lp = padded_len(L);
+            const int seg_lo = (int)(max(gs, st_b) - st_b);
+            const int seg_hi = (int)(min(ge, st_b + lp) - st_b);
+            const bool whole = st_b >= gs && st_b + lp <= ge;
+            const int slot = whole ? -1 : segment_slot(g, st_b, chunk);
+
+            WaveState ws;
+#pragma unroll
+            for (int ct = 0; ct < kOutTiles; ++ct) ws.acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ws.m = -INFINITY;
+            ws.l = 0.f;
+
+            if (active) {
+                const int vis_end = L - p.s_q + tok + 1;  // keys [0, vis_end) visible
+                const int lim = min(seg_hi, vis_end);
+                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
+                const int n_my = nblk > my_kg ? (nblk - my_kg + nkg - 1) / nkg : 0;
+                if (n_my > 0) {
+                    bf16x8 qf[kQkSteps];  // B operand Q^T: lane l -> head l%16, channels 32t + 8(l/16)
+                    const uint16_t *qrow =
+                        p.q + (((int64_t)b * p.s_q + tok) * p.heads + h0 + (lane & 15)) * kDqk +
+                        8 * (lane >> 4);
+#pragma unroll
+                    for (int t = 0; t < kQkSteps; ++t) {
+                        qf[t] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * t);
+                        // Keep Q^T in accumulation registers (the MFMA reads its B
+                        // operand from there): the vector registers stay free for
+                        // the operand reads of the hot loop.
+                        asm volatile("" : "+a"(qf[t]));
+                    }
+
+                    BlockCtx bc;
+                    bc.kv = p.kv;
+                    bc.page_size = p.page_size;
+                    bc.num_pages = p.num_pages;
+                    bc.table_row = p.page_size ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+                    bc.seq_base = (int64_t)b * p.kv_capacity;
+                    bc.last_key = L - 1;
+
+                    const int step = kKeyBlock * nkg;
+                    const int kfirst = seg_lo + kKeyBlock * my_kg;
+                    wait_vm<0>();  // queries and earlier stores are out of the count
+                    issue_block(ring, bc, kfirst, lane);
+                    int i = 0;
+                    for (;;) {
+                        float sv[4], mx = -INFINITY;
+                        bool lagged = false;
+                        for (; i < n_my; ++i) {
+                            if (i + 1 < n_my) {
+                                issue_block(ring + ((i + 1) & 1) * kBlockBytes, bc,
+                                            kfirst + (i + 1) * step, lane);
+                                wait_vm<kQkSteps>();  // block i landed, block i+1 may fly
+                            } else {
+                                wait_vm<0>();
+                            }
+                            const char *stage = ring + (i & 1) * kBlockBytes;
+                            block_scores(sv, mx, stage, qf, kfirst + i * step, vis_end, p.scale_log2,
+                                         lane);
+                            if (__any(mx > ws.m + kMaxLag)) {
+                                lagged = true;
+                                break;
+                            }
+                            block_pv(ws, sv, stage, lane);
+                            wait_lgkm0();  // the stage is refilled two blocks later
+                        }
+                        if (!lagged) break;
+                        // Rare: move the reference max up and rescale, then finish block i.
+                        const float m_new = fmaxf(ws.m, mx);
+                        const float alpha = __builtin_amdgcn_exp2f(ws.m - m_new);
+#pragma unroll
+                        for (int ct = 0; ct < kOutTiles; ++ct) ws.acc[ct] *= alpha;
+                        ws.l *= alpha;
+                        ws.m = m_new;
+                        block_pv(ws, sv, ring + (i & 1) * kBlockBytes, lane);
+                        wait_lgkm0();
+                        ++i;
+                    }
+                }
+            }
+
+            // Merge the waves of this segment through LDS.
+            __syncthreads();
+            if (active) {
+                const int head = lane & 15;
+                const int grp = lane >> 4;
+                float lt = ws.l;
+                lt += __shfl_xor(lt, 16);
+                lt += __shfl_xor(lt, 32);
+                float *dst = merge_o + (wave * 16 + head) * kMergePitch + 4 * grp;
+#pragma unroll
+                for (int ct = 0; ct < kOutTiles; ++ct)
+                    *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct];
+                if (grp == 0) {
+                    merge_m[wave * 16 + head] = ws.m;
+                    merge_l[wave * 16 + head] = lt;
+                }
+            }
+            __syncthreads();
+            {
+                const int head = threadIdx.x >> 4;
+                const int cq = threadIdx.x & 15;
+                for (int rbl = 0; rbl < nrb; ++rbl) {
+                    float M = -INFINITY;
+                    for (int kg = 0; kg < nkg; ++kg) M = fmaxf(M, merge_m[(rbl + nrb * kg) * 16 + head]);
+                    float wgt[kWaves];
+                    float lsum = 0.f;
+#pragma unroll
+                    for (int kg = 0; kg < kWaves; ++kg) {
+                        wgt[kg] = 0.f;
+                        if (kg < nkg) {
+                            const int w = rbl + nrb * kg;
+                            const float mw = merge_m[w * 16 + head];
+                            wgt[kg] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+                            lsum += wgt[kg] * merge_l[w * 16 + head];
+                        }
+                    }
+                    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+                    const float lse2 = lsum > 0.f ? M + log2f(lsum) : -INFINITY;
+                    const int rbg = rb0 + rbl;
+                    const int t = rbg / hpt;
+                    const int hh = (rbg % hpt) * 16 + head;
+                    float *orow;
+                    if (whole) {
+                        orow = p.out + (((int64_t)b * p.s_q + t) * p.heads + hh) * kDv;
+                        if (cq == 0) p.lse[((int64_t)b * p.s_q + t) * p.heads + hh] = lse2 * kLn2;
+                    } else {
+                        const int64_t r = ((int64_t)slot * p.n_rb + rbg) * 16 + head;
+                        orow = p.part_o + r * kDv;
+                        if (cq == 0) p.part_lse[r] = lse2;
+                    }
+#pragma unroll
+                    for (int jc = 0; jc < kDv / 64; ++jc) {
+                        const int c = 4 * cq + 64 * jc;
+                        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kg = 0; kg < kWaves; ++kg) {
+                            if (kg < nkg) {
+                                const int w = rbl + nrb * kg;
+                                o += wgt[kg] * *reinterpret_cast<const f32x4 *>(
+                                                   merge_o + (w * 16 + head) * kMergePitch + c);
+                            }
+                        }
+                        *reinterpret_cast<f32x4 *>(orow + c) = o * inv;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        base = next_base;
+    }
+}
+
+// ------------------------------------------------------------- combine kernel
+
+// grid (batch, n_rb, 512 / kCombineChannels); 256 threads = 16 heads x 16 quads.
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
+    const int b = blockIdx.x;
+    const int rb = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int head = threadIdx.x >> 4;
+    const int c = blockIdx.z * kCombineChannels + 4 * (threadIdx.x & 15);
+
+    const int64_t total = plan_total(p, lane);
+    const int64_t chunk = plan_chunk(total, p.splits, p.min_chunk);
+    int64_t st_b = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+        const int bl = b0 + lane;
+        st_b += wave_sum_i64(bl < b ? padded_len(seq_len(p, bl)) : 0);
+    }
+    const int64_t lp = padded_len(seq_len(p, b));
+    const int hpt = p.heads >> 4;
+    const int t = rb / hpt;
+    const int hh = (rb % hpt) * 16 + head;
+    float *orow = p.out + (((int64_t)b * p.s_q + t) * p.heads + hh) * kDv + c;
+    float *lrow = p.lse + ((int64_t)b * p.s_q + t) * p.heads + hh;
+    if (lp == 0) {  // no key at all: defined empty result
+        *reinterpret_cast<f32x4 *>(orow) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if ((threadIdx.x & 15) == 0 && blockIdx.z == 0) *lrow = -INFINITY;
+        return;
+    }
+    const int g_first = (int)(st_b / chunk);
+    const int g_last = (int)((st_b + lp - 1) / chunk);
+    if (g_first == g_last) return;  // finished inside one range by the split kernel
+
+    float M = -INFINITY;
+    for (int g = g_first; g <= g_last; ++g) {
+        const int slot = segment_slot(g, st_b, chunk);
+        M = fmaxf(M, p.part_lse[((int64_t)slot * p.n_rb + rb) * 16 + head]);
+    }
+    float lsum = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+        for (int g = g_first; g <= g_last; ++g) {
+            const int slot = segment_slot(g, st_b, chunk);
+            const int64_t r = ((int64_t)slot * p.n_rb + rb) * 16 + head;
+            const float lv = p.part_lse[r];
+            if (lv == -INFINITY) continue;
+            const float w = __builtin_amdgcn_exp2f(lv - M);
+            lsum += w;
+            o += w * *reinterpret_cast<const f32x4 *>(p.part_o + r * kDv + c);
+        }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    *reinterpret_cast<f32x4 *>(orow) = o * inv;
+    if ((threadIdx.x & 15) == 0 && blockIdx.z == 0)
+        *lrow = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+}  // namespace mla
+
+// =================================================================== host side
+
+struct mla_ctx {
+    hipStream_t stream = nullptr;
+    int device = 0;
+    int cu_count = 256;
+    int64_t opt_splits = 0;
+    int64_t opt_min_chunk = 256;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    std::string err;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(mla_ctx *ctx, int code, const char *fmt, ...) __attribute__((format(printf, 3, 4)));
+int fail(mla_ctx *ctx, int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (ctx) ctx->err = buf;
+    else g_err = buf;
+    return code;
+}
+
+int hip_fail(mla_ctx *ctx, hipError_t e, const char *what) {
+    return fail(ctx, MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+int check(mla_ctx *ctx, const void *q, const void *kv, const int32_t *block_table,
+          const int32_t *seqlens, float scale, const float *out, const float *lse,
+          const mla_problem *p) {
+    if (!p) return fail(ctx, MLA_ERR_INVALID_ARG, "problem description is NULL");
+    if (!q || !kv || !seqlens || !out || !lse)
+        return fail(ctx, MLA_ERR_INVALID_ARG, "q, kv_cache, seqlens, out and lse must be non-NULL");
+    if (p->batch < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", p->batch);
+    if (p->s_q < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "s_q must be >= 1 (got %d)", p->s_q);
+    if (p->num_heads < 1 || p->num_heads % 16)
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "num_heads must be a positive multiple of 16 (got %d)",
+                    p->num_heads);
+    if (p->head_dim_qk != MLA_HEAD_DIM_QK || p->head_dim_v != MLA_HEAD_DIM_V)
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "head dims must be %d/%d (got %d/%d)", MLA_HEAD_DIM_QK,
+                    MLA_HEAD_DIM_V, p->head_dim_qk, p->head_dim_v);
+    if ((int64_t)p->s_q * p->num_heads > (1 << 20))
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "s_q * num_heads too large");
+    if (!isfinite(scale)) return fail(ctx, MLA_ERR_INVALID_ARG, "scale must be finite");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || ((uintptr_t)lse & 3))
+        return fail(ctx, MLA_ERR_INVALID_ARG,
+                    "q, kv_cache and out must be 16-byte aligned, lse 4-byte aligned");
+    int64_t capacity;
+    if (p->page_size == 0) {
+        if (block_table)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "block_table given but page_size is 0 (contiguous)");
+        if (p->kv_capacity < 1 || p->kv_capacity > (int64_t)INT32_MAX)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "kv_capacity must be in [1, 2^31) (got %lld)",
+                        (long long)p->kv_capacity);
+        capacity = p->kv_capacity;
+    } else {
+        if (p->page_size < 0 || p->page_size % MLA_KEY_BLOCK)
+            return fail(ctx, MLA_ERR_UNSUPPORTED, "page_size must be a positive multiple of %d (got %d)",
+                        MLA_KEY_BLOCK, p->page_size);
+        if (!block_table) return fail(ctx, MLA_ERR_INVALID_ARG, "paged layout needs a block_table");
+        if (p->num_pages < 1 || p->max_pages < 1)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
+        capacity = (int64_t)p->max_pages * p->page_size;
+        if (capacity > (int64_t)INT32_MAX)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "max_pages * page_size must be < 2^31");
+    }
+    if (p->seqlens_host) {
+        for (int b = 0; b < p->batch; ++b) {
+            const int32_t L = p->seqlens_host[b];
+            if (L < p->s_q || (int64_t)L > capacity)
+                return fail(ctx, MLA_ERR_INVALID_ARG,
+                            "seqlens[%d] = %d outside [s_q = %d, capacity = %lld]", b, L, p->s_q,
+                            (long long)capacity);
+        }
+    }
+    return MLA_OK;
+}
+
+int64_t min_chunk_of(const mla_ctx *ctx) { return ctx->opt_min_chunk > 0 ? ctx->opt_min_chunk : 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_version(void) { return "mla_decode 0.1 gfx950"; }
+
+const char *mla_last_error(const mla_ctx *ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+int mla_validate(const void *q, const void *kv_cache, const int32_t *block_table,
+                 const int32_t *seqlens, float scale, const float *out, const float *lse,
+                 const mla_problem *p) {
+    g_err.clear();
+    return check(nullptr, q, kv_cache, block_table, seqlens, scale, out, lse, p);
+}
+
+int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits, int64_t min_chunk,
+             mla_plan_segment *segs, int32_t max_segs, int32_t *n_segs, mla_plan_info *info) {
+    using namespace mla;
+    g_err.clear();
+    if (!seqlens_host || batch < 1 || num_splits < 1 || !n_segs)
+        return fail(nullptr, MLA_ERR_INVALID_ARG, "mla_plan: bad arguments");
+    int64_t total = 0;
+    for (int b = 0; b < batch; ++b) total += padded_len(seqlens_host[b] < 0 ? 0 : seqlens_host[b]);
+    const int64_t chunk = plan_chunk(total, num_splits, min_chunk);
+    int32_t count = 0, split_seqs = 0;
+    int64_t st = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int32_t L = seqlens_host[b] < 0 ? 0 : seqlens_host[b];
+        const int64_t lp = padded_len(L);
+        if (lp == 0) continue;
+        const int g_first = (int)(st / chunk), g_last = (int)((st + lp - 1) / chunk);
+        if (g_first != g_last) ++split_seqs;
+        for (int g = g_first; g <= g_last; ++g) {
+            const int64_t gs = (int64_t)g * chunk, ge = std::min(gs + chunk, total);
+            if (segs && count < max_segs) {
+                mla_plan_segment &s = segs[count];
+                s.group = g;
+                s.seq = b;
+                s.key_begin = (int32_t)(std::max(gs, st) - st);
+                s.key_end = (int32_t)std::min<int64_t>(std::min(ge, st + lp) - st, L);
+                s.slot = g_first == g_last ? -1 : segment_slot(g, st, chunk);
+            }
+            ++count;
+        }
+        st += lp;
+    }
+    *n_segs = count;
+    if (info) {
+        info->chunk = chunk;
+        info->total_keys = total;
+        info->active_groups = (int32_t)((total + chunk - 1) / chunk);
+        info->split_sequences = split_seqs;
+    }
+    if (segs && count > max_segs)
+        return fail(nullptr, MLA_ERR_INVALID_ARG, "mla_plan: %d segments, room for %d", count, max_segs);
+    return MLA_OK;
+}
+
+int mla_ctx_create(mla_ctx **out_ctx, void *stream) {
+    g_err.clear();
+    if (!out_ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx out-pointer is NULL");
+    *out_ctx = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "hipDeviceGetAttribute");
+    mla_ctx *ctx = new (std::nothrow) mla_ctx;
+    if (!ctx) return fail(nullptr, MLA_ERR_WORKSPACE, "out of host memory");
+    ctx->stream = (hipStream_t)stream;
+    ctx->device = dev;
+    ctx->cu_count = cus > 0 ? cus : 256;
+    *out_ctx = ctx;
+    return MLA_OK;
+}
+
+int mla_ctx_destroy(mla_ctx *ctx) {
+    if (!ctx) return MLA_OK;
+    int rc = MLA_OK;
+    if (ctx->ws) {
+        hipError_t e = hipStreamSynchronize(ctx->stream);
+        if (e == hipSuccess) e = hipFree(ctx->ws);
+        if (e != hipSuccess) rc = hip_fail(nullptr, e, "mla_ctx_destroy");
+    }
+    delete ctx;
+    return rc;
+}
+
+int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value) {
+    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
+    switch (option) {
+    case MLA_OPT_NUM_SPLITS:
+        if (value < 0 || value > (1 << 20)) return fail(ctx, MLA_ERR_INVALID_ARG, "bad split count");
+        ctx->opt_splits = value;
+        return MLA_OK;
+    case MLA_OPT_MIN_CHUNK:
+        if (value < 0 || value > ((int64_t)1 << 31)) return fail(ctx, MLA_ERR_INVALID_ARG, "bad min chunk");
+        ctx->opt_min_chunk = value ? value : 256;
+        return MLA_OK;
+    default:
+        return fail(ctx, MLA_ERR_INVALID_ARG, "unknown option %d", option);
+    }
+}
+
+}  // extern "C"
+
+namespace {
+
+int splits_for(const mla_ctx *ctx, int n_rbg) {
+    if (ctx->opt_splits > 0) return (int)ctx->opt_splits;
+    return std::max(1, ctx->cu_count / n_rbg);
+}
+
+size_t workspace_bytes(int splits, int n_rb) {
+    const size_t rows = (size_t)2 * splits * n_rb * 16;
+    return rows * (mla::kDv + 1) * sizeof(float) + 256;
+}
+
+int ensure_workspace(mla_ctx *ctx, size_t need) {
+    if (ctx->ws_bytes >= need) return MLA_OK;
+    if (ctx->ws) {
+        hipError_t e = hipStreamSynchronize(ctx->stream);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
+        e = hipFree(ctx->ws);
+        ctx->ws = nullptr;
+        ctx->ws_bytes = 0;
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipFree");
+    }
+    hipError_t e = hipMalloc(&ctx->ws, need);
+    if (e != hipSuccess) {
+        ctx->ws = nullptr;
+        return fail(ctx, MLA_ERR_WORKSPACE, "hipMalloc(%zu): %s", need, hipGetErrorString(e));
+    }
+    ctx->ws_bytes = need;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads) {
+    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
+    if (s_q < 1 || num_heads < 16 || num_heads % 16)
+        return fail(ctx, MLA_ERR_INVALID_ARG, "bad s_q / num_heads");
+    const int n_rb = s_q * num_heads / 16;
+    const int n_rbg = (n_rb + mla::kWaves - 1) / mla::kWaves;
+    return ensure_workspace(ctx, workspace_bytes(splits_for(ctx, n_rbg), n_rb));
+}
+
+int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t *block_table,
+               const int32_t *seqlens, float scale, float *out, float *lse, const mla_problem *p) {
+    using namespace mla;
+    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->err.clear();
+    int rc = check(ctx, q, kv_cache, block_table, seqlens, scale, out, lse, p);
+    if (rc != MLA_OK) return rc;
+
+    const int n_rb = p->s_q * p->num_heads / 16;
+    const int n_rbg = (n_rb + kWaves - 1) / kWaves;
+    const int splits = splits_for(ctx, n_rbg);
+    rc = ensure_workspace(ctx, workspace_bytes(splits, n_rb));
+    if (rc != MLA_OK) return rc;
+
+    Params prm;
+    prm.q = static_cast<const uint16_t *>(q);
+    prm.kv = static_cast<const uint16_t *>(kv_cache);
+    prm.block_table = p->page_size ? block_table : nullptr;
+    prm.seqlens = seqlens;
+    prm.out = out;
+    prm.lse = lse;
+    prm.part_o = static_cast<float *>(ctx->ws);
+    prm.part_lse = prm.part_o + (size_t)2 * splits * n_rb * 16 * kDv;
+    prm.kv_capacity = p->page_size ? 0 : p->kv_capacity;
+    prm.num_pages = p->page_size ? p->num_pages : 0;
+    prm.capacity = p->page_size ? (int64_t)p->max_pages * p->page_size : p->kv_capacity;
+    prm.min_chunk = min_chunk_of(ctx);
+    prm.batch = p->batch;
+    prm.s_q = p->s_q;
+    prm.heads = p->num_heads;
+    prm.page_size = p->page_size;
+    prm.max_pages = p->page_size ? p->max_pages : 0;
+    prm.n_rb = n_rb;
+    prm.splits = splits;
+    prm.scale_log2 = scale * kLog2e;
+
+    // Launch sizes: with host lengths, only the ranges that hold keys, and
+    // the combine only when some sequence is split.
+    int grid_x = splits;
+    bool need_combine = true;
+    if (p->seqlens_host) {
+        int64_t total = 0;
+        for (int b = 0; b < p->batch; ++b) total += padded_len(p->seqlens_host[b]);
+        const int64_t chunk = plan_chunk(total, splits, prm.min_chunk);
+        grid_x = (int)std::max<int64_t>(1, (total + chunk - 1) / chunk);
+        need_combine = false;
+        int64_t st = 0;
+        for (int b = 0; b < p->batch && !need_combine; ++b) {
+            const int64_t lp = padded_len(p->seqlens_host[b]);
+            need_combine = lp > 0 && st / chunk != (st + lp - 1) / chunk;
+            st += lp;
+        }
+    }
+
+    hipLaunchKernelGGL(mla_split_kernel, dim3(grid_x, n_rbg), dim3(kThreads), 0, ctx->stream, prm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(ctx, e, "mla_split_kernel launch");
+    if (need_combine) {
+        hipLaunchKernelGGL(mla_combine_kernel, dim3(p->batch, n_rb, kDv / kCombineChannels),
+                           dim3(kThreads), 0, ctx->stream, prm);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(ctx, e, "mla_combine_kernel launch");
+    }
+    return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Split-KV plan arithmetic shared by the host mirror (mla_plan) and the
+// kernels, which evaluate it per workgroup from the device seqlens.
+//
+// The keys of all sequences are laid end to end, each sequence padded to a
+// multiple of kKeyBlock, and the line is cut into `splits` equal ranges of
+// `chunk` keys.  Workgroup g owns range [g*chunk, (g+1)*chunk).  A range
+// meets a sequence in a segment.  A sequence inside one range is finished by
+// that workgroup; otherwise every segment writes a partial (normalized O and
+// log2-domain LSE) into slot 2*g + (segment does not start the range) and the
+// combine kernel merges the parts.  Each range holds at most one segment that
+// starts it and one that does not and is partial, so two slots per range
+// suffice.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kKeyBlock = 16;   // keys per wave block
+constexpr int kChunkAlign = kKeyBlock;  // range sizes are multiples of this
+
+__host__ __device__ inline int64_t padded_len(int64_t len) {
+    return (len + kKeyBlock - 1) / kKeyBlock * kKeyBlock;
+}
+
+__host__ __device__ inline int64_t plan_chunk(int64_t total, int32_t splits, int64_t min_chunk) {
+    int64_t per = (total + splits - 1) / splits;
+    int64_t c = per > min_chunk ? per : min_chunk;
+    c = (c + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    return c > 0 ? c : kChunkAlign;
+}
+
+// Partial slot of the segment that sequence starting at `seq_start` has in
+// range g (only meaningful when the sequence is split).
+__host__ __device__ inline int32_t segment_slot(int32_t g, int64_t seq_start, int64_t chunk) {
+    return 2 * g + (seq_start > (int64_t)g * chunk ? 1 : 0);
+}
+
+// Length clamped into what the cache can hold.
+__host__ __device__ inline int32_t clamp_len(int32_t len, int64_t capacity) {
+    if (len < 0) return 0;
+    return (int64_t)len > capacity ? (int32_t)capacity : len;
+}
+
+}  // namespace mla

@@ -1,0 +1,201 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) MLA decode-attention library.
+ *
+ * The operation is the attention step of Multi-head Latent Attention decode
+ * as "FlashMLA-ETAP" states it (gist.science technical summary, Methodology,
+ * the ETAP bullet): S = Q K^T, P = softmax(S), O = P V, over the latent KV
+ * cache that MLA's low-rank joint compression leaves (same summary,
+ * Integration and Implementation): one 576-wide bf16 row per token, shared
+ * by all heads, with K = all 576 channels and V = the first 512 channels of
+ * the same row (head dimension 576: arxivlens page, Limitations).  The
+ * per-GPU shape is 16 heads (technical summary, Problem Statement: 128 heads
+ * over 8 GPUs), a short query and a long context.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are plain pointers to DEVICE memory owned by the caller; the
+ *    library never frees or retains them beyond the call.  Host pointers are
+ *    marked "host".
+ *  - All tensors are dense, row-major, in the element types stated.  bf16 is
+ *    passed as its 16-bit pattern.
+ *  - Return values are mla_status codes; nothing throws across the ABI.  On
+ *    failure mla_last_error() describes the first problem found.
+ *  - Argument checks are host code and run before any HIP call.
+ *  - mla_decode only enqueues work on the context's stream: it never blocks
+ *    the host and, once the context holds enough workspace, never allocates.
+ *  - A context is used by one host thread at a time.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, bad length */
+    MLA_ERR_UNSUPPORTED = -2, /* well-formed but outside what the kernels implement */
+    MLA_ERR_WORKSPACE = -3,   /* workspace allocation failed */
+    MLA_ERR_HIP = -4          /* a HIP runtime call failed */
+} mla_status;
+
+/* Dimensions fixed by the latent layout. */
+#define MLA_HEAD_DIM_QK 576
+#define MLA_HEAD_DIM_V 512
+/* Keys per kernel block: page sizes must be multiples of it. */
+#define MLA_KEY_BLOCK 16
+
+/*
+ * Sizes of one decode call (all counts in elements).
+ *
+ *  batch        B >= 1 sequences.
+ *  s_q          query tokens per sequence, >= 1.  The new tokens are the last
+ *               s_q positions of each sequence, so with s_q > 1 the mask is
+ *               causal: token t (0-based) sees keys 0 .. L_b - s_q + t.
+ *  num_heads    H, a multiple of 16.
+ *  head_dim_qk  must be 576;  head_dim_v must be 512.
+ *  page_size    0 for the contiguous layout; otherwise keys per page, a
+ *               multiple of MLA_KEY_BLOCK.
+ *  kv_capacity  contiguous layout: rows reserved per sequence (the stride
+ *               between sequences is kv_capacity * 576 elements).  Ignored
+ *               when paged.
+ *  num_pages    paged layout: pages in the pool.  Ignored when contiguous.
+ *  max_pages    paged layout: length of a block-table row.
+ *  seqlens_host optional host copy of the device seqlens.  When given, the
+ *               lengths are checked (s_q <= L_b <= capacity) and launches are
+ *               sized to the work; when NULL nothing on the host reads the
+ *               lengths and the kernels clamp them to [0, capacity].
+ */
+typedef struct {
+    int32_t batch;
+    int32_t s_q;
+    int32_t num_heads;
+    int32_t head_dim_qk;
+    int32_t head_dim_v;
+    int32_t page_size;
+    int64_t kv_capacity;
+    int64_t num_pages;
+    int32_t max_pages;
+    const int32_t *seqlens_host;
+} mla_problem;
+
+typedef struct mla_ctx mla_ctx;
+
+/*
+ * Create a context bound to the current HIP device and to `stream` (a
+ * hipStream_t; NULL means the default stream).  The context owns the split
+ * workspace.  Returns MLA_OK and sets *ctx, or an error code.
+ */
+int mla_ctx_create(mla_ctx **ctx, void *stream);
+
+/* Release the context and its workspace (synchronizes its stream first).
+ * NULL is accepted. */
+int mla_ctx_destroy(mla_ctx *ctx);
+
+/*
+ * Make sure the workspace holds the split partials for problems with up to
+ * `s_q` tokens and `num_heads` heads, so that later mla_decode calls of that
+ * size do not allocate.  Allocates with hipMalloc; synchronizes the stream
+ * when it replaces a smaller workspace.
+ */
+int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads);
+
+/*
+ * Tuning knobs (they change speed, never results beyond rounding):
+ *  MLA_OPT_NUM_SPLITS  number of key-range workgroups per row-block group
+ *                      (default: the device's CU count); 0 restores it.
+ *  MLA_OPT_MIN_CHUNK   smallest key range given to one workgroup (default
+ *                      256, rounded up to MLA_KEY_BLOCK).
+ */
+typedef enum { MLA_OPT_NUM_SPLITS = 1, MLA_OPT_MIN_CHUNK = 2 } mla_option;
+int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value);
+
+/* Text of the last error on `ctx` (or of the calling thread's last
+ * context-free call when ctx is NULL).  Never NULL. */
+const char *mla_last_error(const mla_ctx *ctx);
+
+/*
+ * MLA decode attention ("FlashMLA-ETAP", gist.science technical summary,
+ * Methodology: S = Q K^T, P = softmax(S), O = P V), for every sequence b,
+ * query token t and head h:
+ *   s_j      = scale * sum_{c<576} q[b,t,h,c] * kv(b,j)[c]   for visible j
+ *   out[b,t,h,c] = sum_j softmax(s)_j * kv(b,j)[c]           for c < 512
+ *   lse[b,t,h]   = ln sum_j exp(s_j)
+ *
+ *  q            bf16 [B][s_q][H][576], 16-byte aligned.
+ *  kv_cache     bf16, 16-byte aligned; contiguous: [B][kv_capacity][576];
+ *               paged: pool [num_pages][page_size][576].
+ *  block_table  NULL for the contiguous layout; paged: int32
+ *               [B][max_pages], entry j of row b is the pool page holding
+ *               keys j*page_size .. (j+1)*page_size-1 of sequence b.  Entries
+ *               past ceil(L_b / page_size) and cache slots past L_b are
+ *               never read (they may hold anything, NaN included).
+ *  seqlens      int32 [B]: L_b, the number of cached keys including the s_q
+ *               new ones.
+ *  scale        multiplies q.k before the softmax (1/sqrt(576) for MLA).
+ *  out          fp32 [B][s_q][H][512], 16-byte aligned.
+ *  lse          fp32 [B][s_q][H], natural log.
+ *  p            sizes, see mla_problem.
+ *
+ * A row that sees no key (only possible with unchecked lengths L_b < s_q)
+ * gets out = 0 and lse = -inf.  Page ids are clamped into the pool.
+ * Asynchronous on the context's stream.
+ */
+int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache,
+               const int32_t *block_table, const int32_t *seqlens, float scale,
+               float *out, float *lse, const mla_problem *p);
+
+/*
+ * Host-only argument check of mla_decode (the same checks, in the same
+ * order, without a context or any HIP call).  Pointers are only tested for
+ * NULL and alignment.  The message goes to mla_last_error(NULL).
+ */
+int mla_validate(const void *q, const void *kv_cache, const int32_t *block_table,
+                 const int32_t *seqlens, float scale, const float *out,
+                 const float *lse, const mla_problem *p);
+
+/*
+ * The split-KV plan, evaluated on the host exactly as every workgroup
+ * evaluates it on the device.  The keys of all sequences are laid end to end,
+ * each sequence padded to a multiple of MLA_KEY_BLOCK; the line is cut into
+ * `num_splits` equal ranges of `chunk` keys (a multiple of MLA_KEY_BLOCK, at least
+ * `min_chunk`), and workgroup g takes range g.  A workgroup range meets a
+ * sequence in a segment; a sequence that lies inside one range is finished
+ * there, otherwise each segment writes a partial result into slot
+ * 2*g + (segment does not start the range) and a merge combines them.
+ *
+ *  seqlens_host  host int32 [batch].
+ *  segs          host output, room for max_segs segments (may be NULL to
+ *                count only); *n_segs receives the total count.
+ *  info          host output: chunk, total padded keys, active workgroups,
+ *                number of sequences that need the merge.
+ */
+typedef struct {
+    int32_t group;     /* workgroup (key range) index */
+    int32_t seq;       /* sequence b */
+    int32_t key_begin; /* first key of the segment, in sequence b */
+    int32_t key_end;   /* one past the last real key (<= L_b) */
+    int32_t slot;      /* partial slot, or -1 when the segment is the whole sequence */
+} mla_plan_segment;
+
+typedef struct {
+    int64_t chunk;
+    int64_t total_keys;
+    int32_t active_groups;
+    int32_t split_sequences;
+} mla_plan_info;
+
+int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits,
+             int64_t min_chunk, mla_plan_segment *segs, int32_t max_segs,
+             int32_t *n_segs, mla_plan_info *info);
+
+/* Library version string, e.g. "mla_decode 0.1 gfx950". */
+const char *mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DECODE_H */

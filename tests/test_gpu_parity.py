@@ -1,0 +1,164 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bar (fp32 outputs): O RMSE <= 1e-4, O max-abs <= 1e-3, LSE max-abs <= 1e-4.
+Small shapes are checked element by element on every row; the full-size
+workloads on every row where the oracle is quick and on sampled sequences
+otherwise, in the default launch configuration that bench.py times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import compare, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import torch
+
+    import decode_attention_mla_amd as mla
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    c = mla.Context()
+    yield c
+    c.close()
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def oracle_of(inp, rows=None):
+    if rows is None:
+        return oracle.mla_decode(inp.q, inp.kv, inp.block_table, inp.seqlens, inp.scale)
+    bt = None if inp.block_table is None else inp.block_table[rows]
+    kv = inp.kv if inp.block_table is not None else inp.kv[rows]
+    return oracle.mla_decode(inp.q[rows], kv, bt, inp.seqlens[rows], inp.scale)
+
+
+SMALL = [
+    # (B, s_q, H, lens, page_size)
+    (1, 1, 16, [1], 0),
+    (1, 1, 16, [2], 64),
+    (3, 1, 16, [15, 16, 17], 0),
+    (2, 1, 16, [63, 65], 16),
+    (2, 1, 16, [127, 300], 64),
+    (1, 1, 16, [4097], 0),
+    (2, 2, 16, [5, 70], 0),
+    (2, 3, 16, [3, 200], 16),
+    (3, 4, 16, [4, 64, 1000], 64),
+    (2, 1, 32, [100, 33], 0),
+    (2, 1, 64, [257, 16], 16),
+    (1, 4, 32, [129], 64),
+    (4, 2, 48, [31, 32, 33, 500], 0),
+]
+
+
+@pytest.mark.parametrize("splits,min_chunk", [(0, 0), (3, 16), (7, 64), (256, 16)])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_shapes_against_oracle(ctx, case, splits, min_chunk):
+    import decode_attention_mla_amd as mla
+
+    B, s_q, H, lens, ps = SMALL[case]
+    announce(f"small {SMALL[case]} splits={splits} min_chunk={min_chunk}")
+    inp = wl.small("s", B, s_q, H, lens, page_size=ps, seed=100 + case)
+    ctx.set_option(mla.MLA_OPT_NUM_SPLITS, splits)
+    ctx.set_option(mla.MLA_OPT_MIN_CHUNK, min_chunk)
+    try:
+        o, l = run_gpu(ctx, inp)
+        ro, rl = oracle_of(inp)
+        compare(o, l, ro, rl, str(SMALL[case]))
+        # without host lengths the launch is sized blind: same bits
+        o2, l2 = run_gpu(ctx, inp, host_lens=False)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    finally:
+        ctx.set_option(mla.MLA_OPT_NUM_SPLITS, 0)
+        ctx.set_option(mla.MLA_OPT_MIN_CHUNK, 0)
+
+
+def test_single_key_returns_value_row_exactly(ctx):
+    announce("single key")
+    inp = wl.small("one", 4, 1, 16, [1, 1, 1, 1], page_size=64, seed=5)
+    o, l = run_gpu(ctx, inp)
+    for b in range(4):
+        row = wl.bf16_bits_to_f32(inp.kv[inp.block_table[b, 0], 0]).astype(np.float64)
+        assert np.array_equal(o[b, 0], np.broadcast_to(row[:512], (16, 512)))
+    ro, rl = oracle_of(inp)
+    assert np.max(np.abs(l - rl)) <= 1e-5
+
+
+def test_zero_query_gives_mean_of_values(ctx):
+    announce("zero query")
+    inp = wl.small("zq", 2, 4, 16, [77, 1500], seed=6)
+    inp.q[:] = 0
+    o, l = run_gpu(ctx, inp)
+    ro, rl = oracle_of(inp)
+    compare(o, l, ro, rl, "zero query")
+
+
+def test_peaked_softmax_and_large_scores(ctx):
+    """Scaled-up queries give peaked softmaxes and force reference-max moves."""
+    announce("peaked")
+    inp = wl.small("pk", 3, 2, 16, [50, 700, 3000], page_size=16, seed=7)
+    q = wl.bf16_bits_to_f32(inp.q) * 6.0
+    inp.q[:] = wl.f32_to_bf16_bits(q)
+    o, l = run_gpu(ctx, inp)
+    ro, rl = oracle_of(inp)
+    compare(o, l, ro, rl, "peaked")
+
+
+def test_increasing_scores_rescale_every_block(ctx):
+    """Keys whose scores grow along the sequence move the running max in
+    every block (the slow path of the online softmax)."""
+    announce("increasing")
+    inp = wl.small("inc", 1, 1, 16, [2048], seed=8)
+    inp.q[0, 0, :, 520] = wl.f32_to_bf16_bits(np.array([8.0], np.float32))[0]
+    ramp = np.linspace(0, 40, 2048, dtype=np.float32)
+    inp.kv[0, :2048, 520] = wl.f32_to_bf16_bits(ramp)
+    o, l = run_gpu(ctx, inp)
+    ro, rl = oracle_of(inp)
+    compare(o, l, ro, rl, "increasing")
+
+
+def test_bitwise_repeatable(ctx):
+    announce("repeatable")
+    inp = wl.make_inputs(wl.WORKLOADS["mla_bs16_ctx4096"])
+    dev = to_device(inp)
+    o1, l1 = run_gpu(ctx, inp, dev)
+    o2, l2 = run_gpu(ctx, inp, dev)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("mla_bs1_ctx512", None),
+    ("mla_bs16_ctx4096", None),
+    ("mla_bs16_ctx65536", [0, 15]),
+    ("mla_bs64_ragged1k_32k_paged64", [0, 17, 63]),
+    ("mla_bs32_sq4_ctx16384", [0, 31]),
+])
+def test_workload_full_size(ctx, name, rows):
+    import torch
+
+    announce(f"workload {name} rows={rows}")
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, poison=True)
+    o, l = run_gpu(ctx, inp)
+    torch.cuda.empty_cache()
+    ro, rl = oracle_of(inp, rows)
+    sel = slice(None) if rows is None else rows
+    compare(o[sel], l[sel], ro, rl, name)
+    # every row: finite, and the LSE of an N(0,1) context lies near
+    # ln(L) + |scale q|^2 / 2 (the Gaussian tilt law of the inputs)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    a2 = (wl.bf16_bits_to_f32(inp.q).astype(np.float64) * inp.scale) ** 2
+    vis = inp.seqlens[:, None].astype(np.float64) - w.s_q + 1 + np.arange(w.s_q)[None, :]
+    law = np.log(vis)[:, :, None] + a2.sum(-1) / 2
+    tol = 8 * np.sqrt((np.exp(a2.sum(-1)) - 1) / vis[:, :, None])
+    assert np.all(np.abs(l - law) <= tol)

@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark: MLA decode attention on one MI355X.
+
+One step = one mla_decode call (split plan + split kernel + combine kernel)
+over the whole batch, inputs already resident in HBM.  The default workload
+is batch 16, 16 heads, one query token, 65536 cached keys per sequence
+(KV cache 1,207,959,552 B, larger than the 256 MB last-level cache, so every
+step streams it from HBM).  Prints one JSON line.
+
+  value      KV-cache bytes of a step / step time, GB/s (whole job)
+  roofline   the split kernel: algorithmic KV bytes per launch / its mean
+             launch time from HIP events on the stream it runs on, against
+             MI355X's 8 TB/s; traffic from committed rocprofv3 counters when
+             they were taken on the current kernel source, else null
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload on
+             the host cores (a reported baseline, not a target)
+
+Other modes: --workload NAME (any of workloads.WORKLOADS), --calibrate-copy
+(a plain 1 GiB device copy, the reference for the HBM byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV HBM GB/s (% of peak) + µs/call, MLA decode bs16 ctx64K 16 heads"
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("decode_attention_mla_amd/csrc/mla_kernels.hip",
+                  "decode_attention_mla_amd/csrc/plan.h", "include/mla_decode.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per split-kernel launch from committed counter runs, if they
+    were taken on this exact kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_mla_split_{workload}.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None, rec
+    return rec.get("bytes_per_launch"), rec
+
+
+def cpu_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def calibrate_copy(steps: int) -> None:
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"mode": "calibrate-copy", "bytes_read": n, "bytes_written": n,
+                      "ms_per_copy": dt * 1e3, "GBps_read_plus_write": 2 * n / dt / 1e9}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X "
+              "(no collectives); use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decode_attention_mla_amd as mla
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(max(1, args.steps))
+        return 0
+
+    name = args.workload or wl.HEADLINE
+    w = wl.WORKLOADS[name]
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w)
+    kv_bytes = inp.kv_bytes
+    q, kv, bt, lens = wl.to_torch(inp, "cuda:0")
+    # Workloads that fit in the last-level cache rotate over enough copies of
+    # the cache to stream from HBM on every step.
+    copies = [kv]
+    dev_bytes = kv.numel() * 2
+    while dev_bytes * len(copies) < (1 << 30) and len(copies) < 16:
+        copies.append(kv.clone())
+    out = torch.empty((w.batch, w.s_q, w.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.s_q, w.heads), dtype=torch.float32, device="cuda")
+    ctx = mla.Context()
+    ctx.reserve(w.s_q, w.heads)
+
+    def step(i):
+        mla.mla_decode(ctx, q, copies[i % len(copies)], bt, lens, inp.scale, out=out, lse=lse,
+                       seqlens_host=inp.seqlens)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` calls between two synchronizations.
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
+
+    # Per-kernel time of the same steps, HIP events on the library's stream.
+    ctx.kernel_times()
+    ctx.set_option(mla.MLA_OPT_KERNEL_TIMING, 1)
+    for i in range(args.steps):
+        step(i)
+    split_ms, n_split, comb_ms, n_comb = ctx.kernel_times()
+    ctx.set_option(mla.MLA_OPT_KERNEL_TIMING, 0)
+    split_avg_ms = split_ms / max(1, n_split)
+    achieved = kv_bytes / (split_avg_ms * 1e-3) / 1e9
+    traffic, traffic_rec = stored_traffic(name)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16, seeded",
+        "config": {"workload": name, "batch": w.batch, "s_q": w.s_q, "heads": w.heads,
+                   "kv_len": w.seqlen if isinstance(w.seqlen, int) else list(w.seqlen),
+                   "layout": "paged%d" % w.page_size if w.page_size else "contiguous",
+                   "kv_bytes": kv_bytes, "cache_copies_rotated": len(copies)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mla_split_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "split_us_mean": round(split_avg_ms * 1e3, 2),
+            "combine_us_mean": round(comb_ms / n_comb * 1e3, 2) if n_comb else 0.0,
+            "launches_timed": n_split,
+        },
+    }
+    if traffic_rec is not None and traffic is None:
+        res["roofline"]["traffic_note"] = "counters were taken on another kernel source"
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = cpu_threads()
+        # Bounded sample: the first sequence (all heads, all its keys).
+        rows = [0]
+        sample_bytes = int(inp.seqlens[rows].astype(np.int64).sum()) * wl.D_QK * 2
+        bt_s = None if inp.block_table is None else inp.block_table[rows]
+        kv_s = inp.kv if inp.block_table is not None else inp.kv[rows]
+        print(f"[bench] cpu baseline on {threads} threads", file=sys.stderr, flush=True)
+        c0 = time.perf_counter()
+        ro, rl = oracle.mla_decode(inp.q[rows], kv_s, bt_s, inp.seqlens[rows], inp.scale,
+                                   threads=threads)
+        c1 = time.perf_counter()
+        res["cpu_baseline"] = {
+            "value": round(sample_bytes / (c1 - c0) / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"sequence 0 of {name}: {w.s_q * w.heads} rows x {int(inp.seqlens[0])} keys "
+                      f"({sample_bytes} KV bytes), {c1 - c0:.2f} s, fp64",
+        }
+        o = out[rows].cpu().numpy().astype(np.float64)
+        l = lse[rows].cpu().numpy().astype(np.float64)
+        res["parity_sample"] = {
+            "rows": "sequence 0",
+            "o_rmse": float(np.sqrt(np.mean((o - ro) ** 2))),
+            "o_maxabs": float(np.max(np.abs(o - ro))),
+            "lse_maxabs": float(np.max(np.abs(l - rl))),
+        }
+    ctx.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -26,7 +26,7 @@ HEAD_DIM_V = 512
 KEY_BLOCK = 16
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
-MLA_OPT_NUM_SPLITS, MLA_OPT_MIN_CHUNK = 1, 2
+MLA_OPT_NUM_SPLITS, MLA_OPT_MIN_CHUNK, MLA_OPT_KERNEL_TIMING = 1, 2, 3
 
 
 class MlaError(RuntimeError):
@@ -84,9 +84,11 @@ def load() -> ctypes.CDLL:
     lib.mla_validate.argtypes = [P, P, P, P, ctypes.c_float, P, P, ctypes.POINTER(Problem)]
     lib.mla_plan.argtypes = [P, i32, i32, i64, ctypes.POINTER(PlanSegment), i32,
                              ctypes.POINTER(i32), ctypes.POINTER(PlanInfo)]
+    lib.mla_ctx_kernel_times.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     lib.mla_version.restype = ctypes.c_char_p
     for name in ("mla_ctx_create", "mla_ctx_destroy", "mla_ctx_reserve", "mla_ctx_set_option",
-                 "mla_decode", "mla_validate", "mla_plan"):
+                 "mla_decode", "mla_validate", "mla_plan", "mla_ctx_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -153,6 +155,15 @@ class Context:
 
     def set_option(self, option: int, value: int) -> None:
         _check(load().mla_ctx_set_option(self.handle, option, value), self.handle)
+
+    def kernel_times(self):
+        """(split_ms_total, split_launches, combine_ms_total, combine_launches)
+        since the last query; synchronizes the stream."""
+        sm, cm = ctypes.c_double(), ctypes.c_double()
+        sn, cn = ctypes.c_int64(), ctypes.c_int64()
+        _check(load().mla_ctx_kernel_times(self.handle, ctypes.byref(sm), ctypes.byref(sn),
+                                           ctypes.byref(cm), ctypes.byref(cn)), self.handle)
+        return sm.value, sn.value, cm.value, cn.value
 
     def close(self) -> None:
         if self.handle is not None and self.handle.value:

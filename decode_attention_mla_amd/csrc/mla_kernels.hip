@@ -47,6 +47,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "mla_decode.h"
 #include "plan.h"
@@ -62,16 +63,16 @@ constexpr int kVSteps = kDv / 32;              // the first 16 of them are value
 constexpr int kOutTiles = kDv / 16;            // 32 output tiles of 16 channels
 constexpr int kBlockBytes = kKeyBlock * kDqk * 2;         // 18 KB: one 16-key block
 constexpr int kStages = 2;                                 // LDS ring depth per wave
-constexpr int kRingBytes = kWaves * kStages * kBlockBytes; // 144 KB
+constexpr int kStageBytes = kWaves * kBlockBytes;          // one stage of all waves: 72 KB
 constexpr int kMergePitch = kDv + 4;           // floats per merge row (bank spread)
-constexpr int kMergeFloats = kWaves * 16 * kMergePitch;
-constexpr int kStatFloats = kWaves * 16 * 2;   // running max and sum per wave/head
-constexpr int kLdsBytes = (kMergeFloats + kStatFloats) * 4 > kRingBytes
-                              ? (kMergeFloats + kStatFloats) * 4
-                              : kRingBytes;
+constexpr int kMergeWaveFloats = 16 * kMergePitch;          // one wave's O: 33 KB
+static_assert(2 * kMergeWaveFloats * 4 + kWaves * 16 * 2 * 4 <= kStageBytes,
+              "two waves' merge rows and the stats fit in one stage array");
 constexpr int kCombineChannels = 64;           // channels per combine workgroup
+constexpr int kCombineBatch = 16;              // partials merged per round trip
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kNonTemporal = 2;                // cache-policy bits of a streaming load
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -117,6 +118,21 @@ __device__ inline int64_t wave_incl_scan_i64(int64_t v, int lane) {
     return v;
 }
 
+// Values that are the same in every lane, moved to scalar registers so that
+// the compiler treats what depends on them as uniform.
+__device__ inline int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uniform(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ inline int32_t lane_value(int32_t v, int j) { return __builtin_amdgcn_readlane(v, j); }
+__device__ inline int64_t lane_value(int64_t v, int j) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, j);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), j);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ inline int32_t seq_len(const Params &p, int b) {
     return clamp_len(p.seqlens[b], p.capacity);
 }
@@ -128,7 +144,7 @@ __device__ inline int64_t plan_total(const Params &p, int lane) {
         const int b = b0 + lane;
         total += wave_sum_i64(b < p.batch ? padded_len(seq_len(p, b)) : 0);
     }
-    return total;
+    return uniform(total);
 }
 
 __device__ inline uint16_t bf16_bits(float x) {
@@ -166,34 +182,76 @@ struct BlockCtx {
     int32_t last_key;          // L - 1: loads of keys past it are clamped to it
 };
 
-// LDS image of one 16-key block: 18 slices of 1 KB; slice t holds the 16-byte
-// chunks 4t .. 4t+3 (channels 32t .. 32t+31) of the 16 rows, chunk 4t + q of
-// row k at slot 16q + (k ^ 2(q & 1)).  The K operand of QK^T for step t is
-// then one contiguous 1 KB read per wave, and the transposed value reads of
-// PV hit 8 distinct 16-byte bank groups.
-__device__ inline int slot_of(int q, int k) { return 16 * q + (k ^ (2 * (q & 1))); }
+// LDS image of one 16-key block (16 latent rows of 72 16-byte chunks):
+// 18 slices of 1 KB.  Slice t = 9h + u holds rows 8h .. 8h+7, chunks
+// 8u .. 8u+7 (channels 64u .. 64u+63): row 8h + r at slots 8r .. 8r+7,
+// chunk 8u + w at slot 8r + (w ^ swz(r)), swz(r) = 4 bit1(r) + 2 bit2(r).
+// Each direct load then fetches eight whole 128-byte lines, and both operand
+// reads below spread over all LDS banks (the K read of a step hits every
+// 16-byte bank group four times, a V^T read every 8-byte group twice).
+__device__ inline int row_swz(int r) { return 4 * ((r >> 1) & 1) + 2 * ((r >> 2) & 1); }
 
-// Issue the 18 direct-to-LDS 16-byte loads of the block starting at key kb.
-// Lane l of load t fetches row k = (l & 15) ^ 2((l >> 4) & 1), chunk
-// 4t + (l >> 4), and the hardware stores it at slice t, slot l.
+// Issue the 18 direct-to-LDS 16-byte loads of the block starting at key kb,
+// non-temporal (the cache is streamed once).  Lane l of load t = 9h + u
+// fetches row 8h + l/8, chunk 8u + ((l % 8) ^ swz(l/8)); the hardware stores
+// it at slice t, slot l.
 __device__ inline void issue_block(char *stage, const BlockCtx &c, int kb, int lane) {
-    const int q = lane >> 4;
-    const int k = (lane & 15) ^ (2 * (q & 1));
-    const int key = min(kb + k, c.last_key);
-    const uint16_t *row;
-    if (c.page_size) {
-        int64_t page = c.table_row[kb / c.page_size];  // one page per 16-key block
-        page = page < 0 ? 0 : (page >= c.num_pages ? c.num_pages - 1 : page);
-        row = c.kv + (page * c.page_size + key % c.page_size) * (int64_t)kDqk;
-    } else {
-        row = c.kv + (c.seq_base + key) * (int64_t)kDqk;
+    const int r = lane >> 3;
+    const int w = (lane & 7) ^ row_swz(r);
+    const uint16_t *rows[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int key = min(kb + 8 * h + r, c.last_key);
+        if (c.page_size) {
+            int64_t page = c.table_row[kb / c.page_size];  // one page per 16-key block
+            page = page < 0 ? 0 : (page >= c.num_pages ? c.num_pages - 1 : page);
+            rows[h] = c.kv + (page * c.page_size + key % c.page_size) * (int64_t)kDqk + 8 * w;
+        } else {
+            rows[h] = c.kv + (c.seq_base + key) * (int64_t)kDqk + 8 * w;
+        }
     }
-    row += 8 * q;
 #pragma unroll
     for (int t = 0; t < kQkSteps; ++t)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(row + 32 * t),
-                                         (__attribute__((address_space(3))) void *)(stage + t * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(rows[t / 9] + 64 * (t % 9)),
+            (__attribute__((address_space(3))) void *)(stage + t * 1024), 16, 0, kNonTemporal);
+}
+
+// Per-lane byte offsets of the operand reads within a block image.
+//  K operand of QK^T step t (lane l -> key k = l%16, chunk 4t + l/16):
+//    slice 9(k/8) + t/2, slot 8(k%8) + ((4(t%2) + l/16) ^ swz(k%8)),
+//    i.e. k_off[t % 2] + 1024 * (t / 2).
+//  V^T operand of output tile ct (transposing read; in-group lane m of
+//  group g points at key 4g + m/4, channels 16ct + 4(m%4) .. +3: chunk
+//  2ct + (m%4)/2, half m%2):  v_off[ct % 4] + 1024 * (ct / 4).
+struct OperandOffsets {
+    int k_off[2];
+    uint32_t v_off[4];
+};
+
+__device__ inline OperandOffsets operand_offsets(int lane) {
+    OperandOffsets o;
+    {
+        const int k = lane & 15, q = lane >> 4;
+        const int h = k >> 3, r = k & 7;
+        const int r1 = (r >> 1) & 1, r2 = (r >> 2) & 1;
+        const int base = 9 * h * 1024 + 16 * (8 * r + (q ^ (2 * r2)));
+        o.k_off[0] = base + 64 * r1;
+        o.k_off[1] = base + 64 * (1 - r1);
+    }
+    {
+        const int g = lane >> 4, m = lane & 15;
+        const int key = 4 * g + (m >> 2);
+        const int h = key >> 3, r = key & 7;
+        const int r1 = (r >> 1) & 1, r2 = (r >> 2) & 1;
+        const int b = (m & 3) >> 1;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+            o.v_off[c4] = 9 * h * 1024 +
+                          16 * (8 * r + b + 2 * ((c4 & 1) ^ r2) + 4 * (((c4 >> 1) & 1) ^ r1)) +
+                          8 * (m & 1);
+    }
+    return o;
 }
 
 // The compiler does not track completion of direct-to-LDS loads, so the
@@ -214,23 +272,57 @@ __device__ inline void wait_lgkm0() {
     asm volatile("" ::: "memory");
 }
 
-// Scores of one block: S^T[key][head] for 16 keys x 16 heads, scaled into the
-// log2 domain and masked.  Lane l holds head l%16, keys kb + 4(l/16) + i.
-// The A operand (K) comes from the block's LDS image: lane l -> key l%16,
-// channels 32t + 8(l/16) .. +7; the B operand Q^T is in registers.
-__device__ inline void block_scores(float (&sv)[4], float &mx, const char *stage,
-                                    const bf16x8 (&qf)[kQkSteps], int kb, int key_end,
-                                    float scale_log2, int lane) {
-    const int grp = lane >> 4;
-    const char *kop = stage + slot_of(grp, lane & 15) * 16;
-    bf16x8 ka[kQkSteps];  // all K operands first: the reads overlap each other
-#pragma unroll
-    for (int t = 0; t < kQkSteps; ++t) ka[t] = *reinterpret_cast<const bf16x8 *>(kop + t * 1024);
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Eight transposing V^T reads (tiles 8G .. 8G+7; tile ct at
+// v[ct % 4] + 1024 (ct / 4)), waited for inside the same statement so that
+// the outputs are complete when it ends.  (The compiler would otherwise
+// treat such a read as possibly aliasing the in-flight direct-to-LDS loads
+// and wait for those.)
+template <int G>
+__device__ inline void read_vt8(s16x4 (&va)[kOutTiles], const uint32_t (&v)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n"
+        "ds_read_b64_tr_b16 %1, %9 offset:%12\n"
+        "ds_read_b64_tr_b16 %2, %10 offset:%12\n"
+        "ds_read_b64_tr_b16 %3, %11 offset:%12\n"
+        "ds_read_b64_tr_b16 %4, %8 offset:%13\n"
+        "ds_read_b64_tr_b16 %5, %9 offset:%13\n"
+        "ds_read_b64_tr_b16 %6, %10 offset:%13\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(va[8 * G + 0]), "=&v"(va[8 * G + 1]), "=&v"(va[8 * G + 2]), "=&v"(va[8 * G + 3]),
+          "=&v"(va[8 * G + 4]), "=&v"(va[8 * G + 5]), "=&v"(va[8 * G + 6]), "=&v"(va[8 * G + 7])
+        : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "n"(2048 * G), "n"(2048 * G + 1024)
+        : "memory");
+}
+
+// Scores of one block: S^T[key][head] for 16 keys x 16 heads, scaled into
+// the log2 domain and masked; lane l holds head l%16, keys kb + 4(l/16) + i
+// and mx is the block max of its head.  The A operand K comes from the
+// block's LDS image (lane l -> key l%16, channels 32t + 8(l/16) .. +7, one
+// contiguous 1 KB read per wave), the B operand Q^T from registers; two
+// accumulators halve the dependent MFMA chain.  The first eight V^T
+// operands are read here as well.
+__device__ inline void block_scores(float (&sv)[4], float &mx, s16x4 (&va)[kOutTiles],
+                                    const char *stage, const int (&k_off)[2],
+                                    const uint32_t (&v_addr)[4], const bf16x8 (&qf)[kQkSteps],
+                                    int kb, int key_end, float scale_log2, int lane) {
+    bf16x8 ka[kQkSteps];
 #pragma unroll
     for (int t = 0; t < kQkSteps; ++t)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t], qf[t], s, 0, 0, 0);
-    const int k0 = kb + 4 * grp;
+        ka[t] = *reinterpret_cast<const bf16x8 *>(stage + k_off[t & 1] + 1024 * (t >> 1));
+    // All K reads are issued before the first MFMA waits on one of them.
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kQkSteps; t += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t], qf[t], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t + 1], qf[t + 1], s1, 0, 0, 0);
+    }
+    read_vt8<0>(va, v_addr);
+    const f32x4 s = s0 + s1;
+    const int k0 = kb + 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = (k0 + i < key_end) ? s[i] * scale_log2 : -INFINITY;
     mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -238,23 +330,12 @@ __device__ inline void block_scores(float (&sv)[4], float &mx, const char *stage
     mx = fmaxf(mx, __shfl_xor(mx, 32));
 }
 
-// P = exp2(s - m) and O^T += V^T P^T for one block.  P^T is already in the
-// 16x16x16 B layout (lane: head l%16, keys 4(l/16) + i) and is split into
-// bf16 hi + lo parts.  The A operand (V^T: lane l -> channel 16ct + l%16,
-// keys 4(l/16) + i) is read from the block image: channel chunk
-// c = 2ct + (l%16)/8 lives in slice c/4 at slot_of(c%4, key).
-__device__ inline void block_pv(WaveState &st, const float (&sv)[4], const char *stage, int lane) {
-    const int grp = lane >> 4;
-    const int n = lane & 15;
-    s16x4 va[kOutTiles];  // all V^T operands first
-#pragma unroll
-    for (int ct = 0; ct < kOutTiles; ++ct) {
-        const int c = 2 * ct + (n >> 3);
-        const char *base = stage + (c >> 2) * 1024 + ((n & 7) << 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            va[ct][i] = *reinterpret_cast<const short *>(base + slot_of(c & 3, 4 * grp + i) * 16);
-    }
+// P = exp2(s - m) and O^T += V^T P^T.  P^T is already in the 16x16x16 B
+// layout (lane: head l%16, keys 4(l/16) + i) and is split into bf16 hi + lo.
+// The other 24 V^T operands are read eight at a time while the MFMAs of
+// the previous eight run.
+__device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)[kOutTiles],
+                                const uint32_t (&v_addr)[4]) {
     s16x4 phi, plo;
     float psum = 0.f;
 #pragma unroll
@@ -267,9 +348,15 @@ __device__ inline void block_pv(WaveState &st, const float (&sv)[4], const char 
     }
     st.l += psum;
 #pragma unroll
-    for (int ct = 0; ct < kOutTiles; ++ct) {
-        st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], phi, st.acc[ct], 0, 0, 0);
-        st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], plo, st.acc[ct], 0, 0, 0);
+    for (int g = 0; g < kOutTiles / 8; ++g) {
+        if (g == 1) read_vt8<1>(va, v_addr);
+        if (g == 2) read_vt8<2>(va, v_addr);
+        if (g == 3) read_vt8<3>(va, v_addr);
+#pragma unroll
+        for (int ct = 8 * g; ct < 8 * g + 8; ++ct) {
+            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], phi, st.acc[ct], 0, 0, 0);
+            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], plo, st.acc[ct], 0, 0, 0);
+        }
     }
 }
 
@@ -283,10 +370,10 @@ constexpr float kMaxLag = 8.0f;
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_split_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-
+    __shared__ __attribute__((aligned(16))) char ring[kStages * kStageBytes];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // Wave-uniform (scalar) so that stage addresses stay in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = blockIdx.x;
     const int rb0 = blockIdx.y * kWaves;
     const int nrb = min(kWaves, p.n_rb - rb0);
@@ -306,9 +393,16 @@ void mla_split_kernel(Params p) {
     if (gs >= total) return;  // uniform over the workgroup
     const int64_t ge = min(gs + chunk, total);
 
-    char *ring = lds + wave * kStages * kBlockBytes;
-    float *merge_o = reinterpret_cast<float *>(lds);
-    float *merge_m = merge_o + kMergeFloats;
+    char *stage0 = ring + wave * kBlockBytes;
+    char *stage1 = ring + kStageBytes + wave * kBlockBytes;
+    const OperandOffsets offs = operand_offsets(lane);
+    // After a segment the ring holds the waves' O rows for the merge: waves
+    // 0 and 1 in the first stage, waves 2 and 3 (and the stats) in the second.
+    auto merge_row = [&](int w, int head) {
+        return reinterpret_cast<float *>(ring + (w < 2 ? 0 : kStageBytes)) +
+               ((w & 1) * 16 + head) * kMergePitch;
+    };
+    float *merge_m = reinterpret_cast<float *>(ring + kStageBytes) + 2 * kMergeWaveFloats;
     float *merge_l = merge_m + kWaves * 16;
 
     int64_t base = 0;
@@ -319,14 +413,14 @@ void mla_split_kernel(Params p) {
         const int64_t incl = wave_incl_scan_i64(lpl, lane) + base;
         const int64_t stl = incl - lpl;
         uint64_t mask = __ballot(bl < p.batch && lpl > 0 && stl < ge && incl > gs);
-        const int64_t next_base = __shfl(incl, 63);
+        const int64_t next_base = lane_value(incl, 63);
 
         while (mask) {
             const int j = __builtin_ctzll(mask);
             mask &= mask - 1;
             const int b = b0 + j;
-            const int64_t st_b = __shfl(stl, j);
-            const int32_t L = __shfl(Ll, j);
+            const int64_t st_b = lane_value(stl, j);
+            const int32_t L = lane_value(Ll, j);
             const int64_t lp = padded_len(L);
             const int seg_lo = (int)(max(gs, st_b) - st_b);
             const int seg_hi = (int)(min(ge, st_b + lp) - st_b);
@@ -369,28 +463,32 @@ void mla_split_kernel(Params p) {
                     const int step = kKeyBlock * nkg;
                     const int kfirst = seg_lo + kKeyBlock * my_kg;
                     wait_vm<0>();  // queries and earlier stores are out of the count
-                    issue_block(ring, bc, kfirst, lane);
+                    issue_block(stage0, bc, kfirst, lane);
                     int i = 0;
                     for (;;) {
                         float sv[4], mx = -INFINITY;
+                        s16x4 va[kOutTiles];
+                        uint32_t v_addr[4] = {0, 0, 0, 0};
                         bool lagged = false;
                         for (; i < n_my; ++i) {
+                            char *cur = (i & 1) ? stage1 : stage0;
                             if (i + 1 < n_my) {
-                                issue_block(ring + ((i + 1) & 1) * kBlockBytes, bc,
-                                            kfirst + (i + 1) * step, lane);
+                                issue_block((i & 1) ? stage0 : stage1, bc, kfirst + (i + 1) * step, lane);
                                 wait_vm<kQkSteps>();  // block i landed, block i+1 may fly
                             } else {
                                 wait_vm<0>();
                             }
-                            const char *stage = ring + (i & 1) * kBlockBytes;
-                            block_scores(sv, mx, stage, qf, kfirst + i * step, vis_end, p.scale_log2,
-                                         lane);
+#pragma unroll
+                            for (int c4 = 0; c4 < 4; ++c4)
+                                v_addr[c4] = (uint32_t)(uintptr_t)cur + offs.v_off[c4];
+                            block_scores(sv, mx, va, cur, offs.k_off, v_addr, qf, kfirst + i * step,
+                                         vis_end, p.scale_log2, lane);
                             if (__any(mx > ws.m + kMaxLag)) {
                                 lagged = true;
                                 break;
                             }
-                            block_pv(ws, sv, stage, lane);
-                            wait_lgkm0();  // the stage is refilled two blocks later
+                            block_pv(ws, sv, va, v_addr);
+                            wait_lgkm0();  // this stage is refilled by the next block but one
                         }
                         if (!lagged) break;
                         // Rare: move the reference max up and rescale, then finish block i.
@@ -400,7 +498,7 @@ void mla_split_kernel(Params p) {
                         for (int ct = 0; ct < kOutTiles; ++ct) ws.acc[ct] *= alpha;
                         ws.l *= alpha;
                         ws.m = m_new;
-                        block_pv(ws, sv, ring + (i & 1) * kBlockBytes, lane);
+                        block_pv(ws, sv, va, v_addr);
                         wait_lgkm0();
                         ++i;
                     }
@@ -415,7 +513,7 @@ void mla_split_kernel(Params p) {
                 float lt = ws.l;
                 lt += __shfl_xor(lt, 16);
                 lt += __shfl_xor(lt, 32);
-                float *dst = merge_o + (wave * 16 + head) * kMergePitch + 4 * grp;
+                float *dst = merge_row(wave, head) + 4 * grp;
 #pragma unroll
                 for (int ct = 0; ct < kOutTiles; ++ct)
                     *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct];
@@ -465,8 +563,7 @@ void mla_split_kernel(Params p) {
                         for (int kg = 0; kg < kWaves; ++kg) {
                             if (kg < nkg) {
                                 const int w = rbl + nrb * kg;
-                                o += wgt[kg] * *reinterpret_cast<const f32x4 *>(
-                                                   merge_o + (w * 16 + head) * kMergePitch + c);
+                                o += wgt[kg] * *reinterpret_cast<const f32x4 *>(merge_row(w, head) + c);
                             }
                         }
                         *reinterpret_cast<f32x4 *>(orow + c) = o * inv;
@@ -496,6 +593,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
         const int bl = b0 + lane;
         st_b += wave_sum_i64(bl < b ? padded_len(seq_len(p, bl)) : 0);
     }
+    st_b = uniform(st_b);
     const int64_t lp = padded_len(seq_len(p, b));
     const int hpt = p.heads >> 4;
     const int t = rb / hpt;
@@ -511,23 +609,39 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
     const int g_last = (int)((st_b + lp - 1) / chunk);
     if (g_first == g_last) return;  // finished inside one range by the split kernel
 
-    float M = -INFINITY;
-    for (int g = g_first; g <= g_last; ++g) {
-        const int slot = segment_slot(g, st_b, chunk);
-        M = fmaxf(M, p.part_lse[((int64_t)slot * p.n_rb + rb) * 16 + head]);
-    }
-    float lsum = 0.f;
+    // Online merge over the parts, kCombineBatch at a time: all loads of a
+    // batch are issued before any is used, so a batch costs one round trip.
+    const int n_parts = g_last - g_first + 1;
+    float M = -INFINITY, lsum = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-        for (int g = g_first; g <= g_last; ++g) {
-            const int slot = segment_slot(g, st_b, chunk);
-            const int64_t r = ((int64_t)slot * p.n_rb + rb) * 16 + head;
-            const float lv = p.part_lse[r];
-            if (lv == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f(lv - M);
-            lsum += w;
-            o += w * *reinterpret_cast<const f32x4 *>(p.part_o + r * kDv + c);
+    for (int k0 = 0; k0 < n_parts; k0 += kCombineBatch) {
+        float lv[kCombineBatch];
+        f32x4 ov[kCombineBatch];
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            const int g = g_first + min(k0 + k, n_parts - 1);
+            const int64_t r = ((int64_t)segment_slot(g, st_b, chunk) * p.n_rb + rb) * 16 + head;
+            lv[k] = p.part_lse[r];
+            ov[k] = *reinterpret_cast<const f32x4 *>(p.part_o + r * kDv + c);
         }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            if (k0 + k >= n_parts) lv[k] = -INFINITY;
+            mb = fmaxf(mb, lv[k]);
+        }
+        const float m_new = fmaxf(M, mb);
+        if (m_new == -INFINITY) continue;  // no key in any part so far
+        const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+        lsum *= alpha;
+        o *= alpha;
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            const float w = __builtin_amdgcn_exp2f(lv[k] - m_new);  // 0 for -inf parts
+            lsum += w;
+            o += w * ov[k];
+        }
+        M = m_new;
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     *reinterpret_cast<f32x4 *>(orow) = o * inv;
@@ -545,9 +659,17 @@ struct mla_ctx {
     int cu_count = 256;
     int64_t opt_splits = 0;
     int64_t opt_min_chunk = 256;
+    bool timing = false;
     void *ws = nullptr;
     size_t ws_bytes = 0;
     std::string err;
+    // Event pairs around recorded launches: kind 0 = split, 1 = combine.
+    struct Timed {
+        hipEvent_t start, stop;
+        int kind;
+    };
+    std::vector<Timed> timed;
+    std::vector<hipEvent_t> spare;
 };
 
 namespace {
@@ -710,6 +832,11 @@ int mla_ctx_destroy(mla_ctx *ctx) {
         if (e == hipSuccess) e = hipFree(ctx->ws);
         if (e != hipSuccess) rc = hip_fail(nullptr, e, "mla_ctx_destroy");
     }
+    for (auto &t : ctx->timed) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+    }
+    for (auto e : ctx->spare) (void)hipEventDestroy(e);
     delete ctx;
     return rc;
 }
@@ -725,6 +852,9 @@ int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value) {
         if (value < 0 || value > ((int64_t)1 << 31)) return fail(ctx, MLA_ERR_INVALID_ARG, "bad min chunk");
         ctx->opt_min_chunk = value ? value : 256;
         return MLA_OK;
+    case MLA_OPT_KERNEL_TIMING:
+        ctx->timing = value != 0;
+        return MLA_OK;
     default:
         return fail(ctx, MLA_ERR_INVALID_ARG, "unknown option %d", option);
     }
@@ -733,6 +863,35 @@ int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value) {
 }  // extern "C"
 
 namespace {
+
+hipError_t take_event(mla_ctx *ctx, hipEvent_t *e) {
+    if (!ctx->spare.empty()) {
+        *e = ctx->spare.back();
+        ctx->spare.pop_back();
+        return hipSuccess;
+    }
+    return hipEventCreate(e);
+}
+
+// Record an event pair around one launch when timing is on.
+struct LaunchTimer {
+    mla_ctx *ctx;
+    int kind;
+    hipEvent_t start = nullptr, stop = nullptr;
+    LaunchTimer(mla_ctx *c, int k) : ctx(c), kind(k) {
+        if (!ctx->timing) return;
+        if (take_event(ctx, &start) != hipSuccess || take_event(ctx, &stop) != hipSuccess) {
+            ctx->timing = false;
+            return;
+        }
+        (void)hipEventRecord(start, ctx->stream);
+    }
+    void done() {
+        if (!start) return;
+        (void)hipEventRecord(stop, ctx->stream);
+        ctx->timed.push_back({start, stop, kind});
+    }
+};
 
 int splits_for(const mla_ctx *ctx, int n_rbg) {
     if (ctx->opt_splits > 0) return (int)ctx->opt_splits;
@@ -830,15 +989,43 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t 
         }
     }
 
+    LaunchTimer t_split(ctx, 0);
     hipLaunchKernelGGL(mla_split_kernel, dim3(grid_x, n_rbg), dim3(kThreads), 0, ctx->stream, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(ctx, e, "mla_split_kernel launch");
+    t_split.done();
     if (need_combine) {
+        LaunchTimer t_comb(ctx, 1);
         hipLaunchKernelGGL(mla_combine_kernel, dim3(p->batch, n_rb, kDv / kCombineChannels),
                            dim3(kThreads), 0, ctx->stream, prm);
         e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(ctx, e, "mla_combine_kernel launch");
+        t_comb.done();
     }
+    return MLA_OK;
+}
+
+int mla_ctx_kernel_times(mla_ctx *ctx, double *split_ms, int64_t *split_launches,
+                         double *combine_ms, int64_t *combine_launches) {
+    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
+    hipError_t e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
+    double ms[2] = {0.0, 0.0};
+    int64_t n[2] = {0, 0};
+    for (auto &t : ctx->timed) {
+        float v = 0.f;
+        e = hipEventElapsedTime(&v, t.start, t.stop);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipEventElapsedTime");
+        ms[t.kind] += v;
+        n[t.kind] += 1;
+        ctx->spare.push_back(t.start);
+        ctx->spare.push_back(t.stop);
+    }
+    ctx->timed.clear();
+    if (split_ms) *split_ms = ms[0];
+    if (split_launches) *split_launches = n[0];
+    if (combine_ms) *combine_ms = ms[1];
+    if (combine_launches) *combine_launches = n[1];
     return MLA_OK;
 }
 

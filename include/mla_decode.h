@@ -109,9 +109,24 @@ int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads);
  *                      (default: the device's CU count); 0 restores it.
  *  MLA_OPT_MIN_CHUNK   smallest key range given to one workgroup (default
  *                      256, rounded up to MLA_KEY_BLOCK).
+ *  MLA_OPT_KERNEL_TIMING  1: bracket every kernel launch with HIP events on
+ *                      the context's stream (see mla_ctx_kernel_times); 0: off.
  */
-typedef enum { MLA_OPT_NUM_SPLITS = 1, MLA_OPT_MIN_CHUNK = 2 } mla_option;
+typedef enum {
+    MLA_OPT_NUM_SPLITS = 1,
+    MLA_OPT_MIN_CHUNK = 2,
+    MLA_OPT_KERNEL_TIMING = 3
+} mla_option;
 int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value);
+
+/*
+ * Per-kernel device time of the launches made since the last query while
+ * MLA_OPT_KERNEL_TIMING was on: total milliseconds of the split kernel and
+ * of the combine kernel, and how many of each ran.  Synchronizes the
+ * context's stream, then forgets the recorded launches.
+ */
+int mla_ctx_kernel_times(mla_ctx *ctx, double *split_ms, int64_t *split_launches,
+                         double *combine_ms, int64_t *combine_launches);
 
 /* Text of the last error on `ctx` (or of the calling thread's last
  * context-free call when ctx is NULL).  Never NULL. */

@@ -13,14 +13,7 @@ LSE_MAXABS_MAX = 1e-4
 
 
 def to_device(inp: wl.Inputs):
-    import torch
-
-    dev = torch.device("cuda:0")
-    q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
-    kv = torch.from_numpy(inp.kv.view(np.int16)).to(dev).view(torch.bfloat16)
-    bt = None if inp.block_table is None else torch.from_numpy(inp.block_table).to(dev)
-    lens = torch.from_numpy(inp.seqlens).to(dev)
-    return q, kv, bt, lens
+    return wl.to_torch(inp, "cuda:0")
 
 
 def run_gpu(ctx, inp: wl.Inputs, dev=None, host_lens=True, out=None, lse=None):

@@ -164,6 +164,18 @@ def make_inputs(
     return Inputs(w, q, pool, table, lens, w.scale)
 
 
+def to_torch(inp: Inputs, device="cuda:0"):
+    """Upload the arrays as torch tensors (bf16 views of the bit patterns)."""
+    import torch
+
+    dev = torch.device(device)
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kv = torch.from_numpy(inp.kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = None if inp.block_table is None else torch.from_numpy(inp.block_table).to(dev)
+    lens = torch.from_numpy(inp.seqlens).to(dev)
+    return q, kv, bt, lens
+
+
 def small(name: str, batch: int, s_q: int, heads: int, seqlens: Sequence[int],
           page_size: int = 0, seed: int = 7) -> Inputs:
     """A small test shape with explicit per-sequence lengths."""

@@ -64,6 +64,13 @@ constexpr int kOutTiles = kDv / 16;            // 32 output tiles of 16 channels
 constexpr int kBlockBytes = kKeyBlock * kDqk * 2;         // 18 KB: one 16-key block
 constexpr int kStages = 2;                                 // LDS ring depth per wave
 constexpr int kStageBytes = kWaves * kBlockBytes;          // one stage of all waves: 72 KB
+// Shared rings (several row blocks per workgroup): slots per key group.  At
+// most three blocks may be in flight behind the one waited for (the 6-bit
+// vector-memory counter holds 63 loads).
+constexpr int kSharedStages1 = 5;  // one key group
+constexpr int kSharedStages2 = 4;  // two key groups
+static_assert(kSharedStages1 * kBlockBytes <= kStages * kStageBytes, "ring size");
+static_assert(2 * kSharedStages2 * kBlockBytes <= kStages * kStageBytes, "ring size");
 constexpr int kMergePitch = kDv + 4;           // floats per merge row (bank spread)
 constexpr int kMergeWaveFloats = 16 * kMergePitch;          // one wave's O: 33 KB
 static_assert(2 * kMergeWaveFloats * 4 + kWaves * 16 * 2 * 4 <= kStageBytes,
@@ -360,6 +367,28 @@ __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)
     }
 }
 
+// Move the reference max up to the block max and rescale (rare path).
+__device__ inline void rescale(WaveState &ws, float mx) {
+    const float m_new = fmaxf(ws.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(ws.m - m_new);
+#pragma unroll
+    for (int ct = 0; ct < kOutTiles; ++ct) ws.acc[ct] *= alpha;
+    ws.l *= alpha;
+    ws.m = m_new;
+}
+
+// Wait until at most n blocks (18 loads each, n <= 3) are in flight.
+__device__ inline void wait_vm_blocks(int n) {
+    if (n <= 0)
+        wait_vm<0>();
+    else if (n == 1)
+        wait_vm<kQkSteps>();
+    else if (n == 2)
+        wait_vm<2 * kQkSteps>();
+    else
+        wait_vm<3 * kQkSteps>();
+}
+
 // The running max m is only a reference point: P = exp2(s - m) may exceed 1
 // as long as s - m <= kMaxLag, so the accumulators are rescaled only when a
 // block's max passes m + kMaxLag (and for the first block).  The result is
@@ -393,8 +422,6 @@ void mla_split_kernel(Params p) {
     if (gs >= total) return;  // uniform over the workgroup
     const int64_t ge = min(gs + chunk, total);
 
-    char *stage0 = ring + wave * kBlockBytes;
-    char *stage1 = ring + kStageBytes + wave * kBlockBytes;
     const OperandOffsets offs = operand_offsets(lane);
     // After a segment the ring holds the waves' O rows for the merge: waves
     // 0 and 1 in the first stage, waves 2 and 3 (and the stats) in the second.
@@ -433,75 +460,125 @@ void mla_split_kernel(Params p) {
             ws.m = -INFINITY;
             ws.l = 0.f;
 
+            BlockCtx bc;
+            bc.kv = p.kv;
+            bc.page_size = p.page_size;
+            bc.num_pages = p.num_pages;
+            bc.table_row = p.page_size ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+            bc.seq_base = (int64_t)b * p.kv_capacity;
+            bc.last_key = L - 1;
+            const int vis_end = L - p.s_q + tok + 1;  // keys [0, vis_end) visible to this wave
+            bf16x8 qf[kQkSteps];  // B operand Q^T: lane l -> head l%16, channels 32t + 8(l/16)
             if (active) {
-                const int vis_end = L - p.s_q + tok + 1;  // keys [0, vis_end) visible
+                const uint16_t *qrow =
+                    p.q + (((int64_t)b * p.s_q + tok) * p.heads + h0 + (lane & 15)) * kDqk +
+                    8 * (lane >> 4);
+#pragma unroll
+                for (int t = 0; t < kQkSteps; ++t) {
+                    qf[t] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * t);
+                    // Keep Q^T in accumulation registers (the MFMA reads its B
+                    // operand from there): the vector registers stay free for the
+                    // operand reads of the hot loop.
+                    asm volatile("" : "+a"(qf[t]));
+                }
+            }
+            wait_vm<0>();  // queries and earlier stores are out of the count
+
+            if (nrb == 1) {
+                // One row block: each wave streams its own blocks (every
+                // kWaves-th one) through a private two-stage ring, no barrier.
                 const int lim = min(seg_hi, vis_end);
                 const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
                 const int n_my = nblk > my_kg ? (nblk - my_kg + nkg - 1) / nkg : 0;
-                if (n_my > 0) {
-                    bf16x8 qf[kQkSteps];  // B operand Q^T: lane l -> head l%16, channels 32t + 8(l/16)
-                    const uint16_t *qrow =
-                        p.q + (((int64_t)b * p.s_q + tok) * p.heads + h0 + (lane & 15)) * kDqk +
-                        8 * (lane >> 4);
+                const int step = kKeyBlock * nkg;
+                const int kfirst = seg_lo + kKeyBlock * my_kg;
+                char *stage0 = ring + wave * kBlockBytes;
+                char *stage1 = ring + kStageBytes + wave * kBlockBytes;
+                if (n_my > 0) issue_block(stage0, bc, kfirst, lane);
+                int i = 0;
+                for (;;) {
+                    float sv[4], mx = -INFINITY;
+                    s16x4 va[kOutTiles];
+                    uint32_t v_addr[4] = {0, 0, 0, 0};
+                    bool lagged = false;
+                    for (; i < n_my; ++i) {
+                        char *cur = (i & 1) ? stage1 : stage0;
+                        if (i + 1 < n_my) {
+                            issue_block((i & 1) ? stage0 : stage1, bc, kfirst + (i + 1) * step, lane);
+                            wait_vm<kQkSteps>();  // block i landed, block i+1 may fly
+                        } else {
+                            wait_vm<0>();
+                        }
 #pragma unroll
-                    for (int t = 0; t < kQkSteps; ++t) {
-                        qf[t] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * t);
-                        // Keep Q^T in accumulation registers (the MFMA reads its B
-                        // operand from there): the vector registers stay free for
-                        // the operand reads of the hot loop.
-                        asm volatile("" : "+a"(qf[t]));
+                        for (int c4 = 0; c4 < 4; ++c4)
+                            v_addr[c4] = (uint32_t)(uintptr_t)cur + offs.v_off[c4];
+                        block_scores(sv, mx, va, cur, offs.k_off, v_addr, qf, kfirst + i * step,
+                                     vis_end, p.scale_log2, lane);
+                        if (__any(mx > ws.m + kMaxLag)) {
+                            lagged = true;
+                            break;
+                        }
+                        block_pv(ws, sv, va, v_addr);
+                        wait_lgkm0();  // this stage is refilled by the next block but one
                     }
-
-                    BlockCtx bc;
-                    bc.kv = p.kv;
-                    bc.page_size = p.page_size;
-                    bc.num_pages = p.num_pages;
-                    bc.table_row = p.page_size ? p.block_table + (int64_t)b * p.max_pages : nullptr;
-                    bc.seq_base = (int64_t)b * p.kv_capacity;
-                    bc.last_key = L - 1;
-
-                    const int step = kKeyBlock * nkg;
-                    const int kfirst = seg_lo + kKeyBlock * my_kg;
-                    wait_vm<0>();  // queries and earlier stores are out of the count
-                    issue_block(stage0, bc, kfirst, lane);
-                    int i = 0;
-                    for (;;) {
-                        float sv[4], mx = -INFINITY;
-                        s16x4 va[kOutTiles];
-                        uint32_t v_addr[4] = {0, 0, 0, 0};
-                        bool lagged = false;
-                        for (; i < n_my; ++i) {
-                            char *cur = (i & 1) ? stage1 : stage0;
-                            if (i + 1 < n_my) {
-                                issue_block((i & 1) ? stage0 : stage1, bc, kfirst + (i + 1) * step, lane);
-                                wait_vm<kQkSteps>();  // block i landed, block i+1 may fly
-                            } else {
-                                wait_vm<0>();
-                            }
+                    if (!lagged) break;
+                    rescale(ws, mx);
+                    block_pv(ws, sv, va, v_addr);
+                    wait_lgkm0();
+                    ++i;
+                }
+            } else {
+                // Several row blocks: the waves of a key group (same blocks,
+                // different row blocks) share each block.  One producer wave
+                // per key group loads it into a deeper shared ring; a barrier
+                // per block publishes it and frees the slot read one block ago.
+                const int S = nkg == 1 ? kSharedStages1 : kSharedStages2;
+                const int kgq = active ? my_kg : 0;
+                const int tok_last = (rb0 + nrb - 1) / hpt;  // sees the most keys
+                const int lim = min(seg_hi, L - p.s_q + tok_last + 1);
+                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
+                const int n_iter = (nblk + nkg - 1) / nkg;  // same in every wave
+                const int n_kg = nblk > kgq ? (nblk - kgq + nkg - 1) / nkg : 0;
+                const bool producer = active && my_rbl == 0;
+                const int step = kKeyBlock * nkg;
+                const int kfirst = seg_lo + kKeyBlock * kgq;
+                char *slots = ring + kgq * S * kBlockBytes;
+                if (producer)
+                    for (int s = 0; s < S - 1 && s < n_kg; ++s)
+                        issue_block(slots + s * kBlockBytes, bc, kfirst + s * step, lane);
+                int i = 0;
+                for (;;) {
+                    float sv[4], mx = -INFINITY;
+                    s16x4 va[kOutTiles];
+                    uint32_t v_addr[4] = {0, 0, 0, 0};
+                    bool lagged = false;
+                    for (; i < n_iter; ++i) {
+                        if (producer) wait_vm_blocks(min(S - 2, n_kg - 1 - i));
+                        __syncthreads();  // block i is in; every wave is done with block i-1
+                        if (producer && i + S - 1 < n_kg)
+                            issue_block(slots + ((i + S - 1) % S) * kBlockBytes, bc,
+                                        kfirst + (i + S - 1) * step, lane);
+                        const int kb = kfirst + i * step;
+                        if (active && i < n_kg && kb < vis_end) {
+                            char *cur = slots + (i % S) * kBlockBytes;
 #pragma unroll
                             for (int c4 = 0; c4 < 4; ++c4)
                                 v_addr[c4] = (uint32_t)(uintptr_t)cur + offs.v_off[c4];
-                            block_scores(sv, mx, va, cur, offs.k_off, v_addr, qf, kfirst + i * step,
-                                         vis_end, p.scale_log2, lane);
+                            block_scores(sv, mx, va, cur, offs.k_off, v_addr, qf, kb, vis_end,
+                                         p.scale_log2, lane);
                             if (__any(mx > ws.m + kMaxLag)) {
                                 lagged = true;
                                 break;
                             }
                             block_pv(ws, sv, va, v_addr);
-                            wait_lgkm0();  // this stage is refilled by the next block but one
                         }
-                        if (!lagged) break;
-                        // Rare: move the reference max up and rescale, then finish block i.
-                        const float m_new = fmaxf(ws.m, mx);
-                        const float alpha = __builtin_amdgcn_exp2f(ws.m - m_new);
-#pragma unroll
-                        for (int ct = 0; ct < kOutTiles; ++ct) ws.acc[ct] *= alpha;
-                        ws.l *= alpha;
-                        ws.m = m_new;
-                        block_pv(ws, sv, va, v_addr);
                         wait_lgkm0();
-                        ++i;
                     }
+                    if (!lagged) break;
+                    rescale(ws, mx);
+                    block_pv(ws, sv, va, v_addr);
+                    wait_lgkm0();
+                    ++i;
                 }
             }
 

@@ -64,13 +64,10 @@ constexpr int kOutTiles = kDv / 16;            // 32 output tiles of 16 channels
 constexpr int kBlockBytes = kKeyBlock * kDqk * 2;         // 18 KB: one 16-key block
 constexpr int kStages = 2;                                 // LDS ring depth per wave
 constexpr int kStageBytes = kWaves * kBlockBytes;          // one stage of all waves: 72 KB
-// Shared rings (several row blocks per workgroup): slots per key group.  At
-// most three blocks may be in flight behind the one waited for (the 6-bit
-// vector-memory counter holds 63 loads).
-constexpr int kSharedStages1 = 5;  // one key group
-constexpr int kSharedStages2 = 4;  // two key groups
-static_assert(kSharedStages1 * kBlockBytes <= kStages * kStageBytes, "ring size");
-static_assert(2 * kSharedStages2 * kBlockBytes <= kStages * kStageBytes, "ring size");
+// Shared rings (several row blocks per workgroup): per key group two 32-key
+// steps of two blocks each, one computed while the next is in flight.
+constexpr int kPairSlots = 4;
+static_assert(2 * kPairSlots * kBlockBytes <= kStages * kStageBytes, "ring size");
 constexpr int kMergePitch = kDv + 4;           // floats per merge row (bank spread)
 constexpr int kMergeWaveFloats = 16 * kMergePitch;          // one wave's O: 33 KB
 static_assert(2 * kMergeWaveFloats * 4 + kWaves * 16 * 2 * 4 <= kStageBytes,
@@ -273,6 +270,16 @@ __device__ inline void wait_vm() {
     asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier without the memory fence of __syncthreads: that fence
+// would wait for every outstanding load, including the direct loads of the
+// next step.  Used only where each wave has already waited explicitly for
+// what the others need (its share of direct loads, its own LDS reads).
+__device__ inline void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ inline void wait_lgkm0() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (0x7 << 4));
@@ -367,6 +374,107 @@ __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)
     }
 }
 
+// Sixteen transposing V^T reads: tiles 4G .. 4G+3 of blocks A and B (bases
+// vA / vB as in read_vt8), waited for inside the statement.
+template <int G>
+__device__ inline void read_vt_pair4(s16x4 (&va)[kOutTiles], s16x4 (&vb)[kOutTiles],
+                                     const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(va[4 * G + 0]), "=&v"(va[4 * G + 1]), "=&v"(va[4 * G + 2]), "=&v"(va[4 * G + 3]),
+          "=&v"(vb[4 * G + 0]), "=&v"(vb[4 * G + 1]), "=&v"(vb[4 * G + 2]), "=&v"(vb[4 * G + 3])
+        : "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "v"(vB[0]), "v"(vB[1]), "v"(vB[2]),
+          "v"(vB[3]), "n"(1024 * G)
+        : "memory");
+}
+
+// ---- 32-key steps (shared rings): two 16-key blocks A and B per step ----
+//
+// Scores of both blocks (sv[0..3] from A, sv[4..7] from B, lane l: head
+// l%16, keys 4(l/16) + i of each block) and their joint max.
+__device__ inline void pair_scores(float (&sv)[8], float &mx, const char *stA, const char *stB,
+                                   const int (&k_off)[2], const bf16x8 (&qf)[kQkSteps], int kbA,
+                                   int kbB, int key_end, float scale_log2, int lane) {
+    bf16x8 ka[2][kQkSteps];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < kQkSteps; ++t)
+            ka[h][t] = *reinterpret_cast<const bf16x8 *>((h ? stB : stA) + k_off[t & 1] +
+                                                         1024 * (t >> 1));
+    // All 36 K reads are issued before the first MFMA waits on one of them.
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kQkSteps; t += 2) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][t], qf[t], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][t + 1], qf[t + 1], s1, 0, 0, 0);
+        }
+        s[h] = s0 + s1;
+    }
+    const int kA = kbA + 4 * (lane >> 4), kB = kbB + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sv[i] = (kA + i < key_end) ? s[0][i] * scale_log2 : -INFINITY;
+        sv[4 + i] = (kB + i < key_end) ? s[1][i] * scale_log2 : -INFINITY;
+    }
+    mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// O^T += V^T P^T over 32 keys with 16x16x32 MFMAs.  Both operands use the
+// same k order: slot 8(l/16) + i is key 4(l/16) + i of block A for i < 4 and
+// key 4(l/16) + i - 4 of block B for i >= 4.  P^T (B operand) is the
+// joined score registers; V^T (A operand) joins one transposing read of
+// each block.
+__device__ inline void pair_pv(WaveState &st, const float (&sv)[8], const uint32_t (&vA)[4],
+                               const uint32_t (&vB)[4]) {
+    bf16x8 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(sv[i] - st.m);
+        psum += pr;
+        const __bf16 h = static_cast<__bf16>(pr);
+        phi[i] = h;
+        plo[i] = static_cast<__bf16>(pr - static_cast<float>(h));
+    }
+    st.l += psum;
+    s16x4 va[kOutTiles], vb[kOutTiles];
+#pragma unroll
+    for (int g = 0; g < kOutTiles / 4; ++g) {
+        if (g == 0) read_vt_pair4<0>(va, vb, vA, vB);
+        if (g == 1) read_vt_pair4<1>(va, vb, vA, vB);
+        if (g == 2) read_vt_pair4<2>(va, vb, vA, vB);
+        if (g == 3) read_vt_pair4<3>(va, vb, vA, vB);
+        if (g == 4) read_vt_pair4<4>(va, vb, vA, vB);
+        if (g == 5) read_vt_pair4<5>(va, vb, vA, vB);
+        if (g == 6) read_vt_pair4<6>(va, vb, vA, vB);
+        if (g == 7) read_vt_pair4<7>(va, vb, vA, vB);
+#pragma unroll
+        for (int ct = 4 * g; ct < 4 * g + 4; ++ct) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(va[ct], vb[ct], 0, 1, 2, 3, 4, 5, 6, 7));
+            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[ct], 0, 0, 0);
+            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[ct], 0, 0, 0);
+        }
+    }
+}
+
 // Move the reference max up to the block max and rescale (rare path).
 __device__ inline void rescale(WaveState &ws, float mx) {
     const float m_new = fmaxf(ws.m, mx);
@@ -375,18 +483,6 @@ __device__ inline void rescale(WaveState &ws, float mx) {
     for (int ct = 0; ct < kOutTiles; ++ct) ws.acc[ct] *= alpha;
     ws.l *= alpha;
     ws.m = m_new;
-}
-
-// Wait until at most n blocks (18 loads each, n <= 3) are in flight.
-__device__ inline void wait_vm_blocks(int n) {
-    if (n <= 0)
-        wait_vm<0>();
-    else if (n == 1)
-        wait_vm<kQkSteps>();
-    else if (n == 2)
-        wait_vm<2 * kQkSteps>();
-    else
-        wait_vm<3 * kQkSteps>();
 }
 
 // The running max m is only a reference point: P = exp2(s - m) may exceed 1
@@ -482,7 +578,10 @@ void mla_split_kernel(Params p) {
                     asm volatile("" : "+a"(qf[t]));
                 }
             }
-            wait_vm<0>();  // queries and earlier stores are out of the count
+            // No wait here: the query loads (and the previous segment's
+            // stores) are older than every direct load issued below, and the
+            // vector-memory counter drains in order, so each block wait also
+            // covers them.
 
             if (nrb == 1) {
                 // One row block: each wave streams its own blocks (every
@@ -528,55 +627,66 @@ void mla_split_kernel(Params p) {
                     ++i;
                 }
             } else {
-                // Several row blocks: the waves of a key group (same blocks,
-                // different row blocks) share each block.  One producer wave
-                // per key group loads it into a deeper shared ring; a barrier
-                // per block publishes it and frees the slot read one block ago.
-                const int S = nkg == 1 ? kSharedStages1 : kSharedStages2;
+                // Several row blocks: the waves of a key group (same keys,
+                // different row blocks) share each 32-key step, two 16-key
+                // blocks.  One producer wave per key group loads it into a
+                // shared ring of two steps; a barrier per step publishes it
+                // and frees the slots read one step ago.
                 const int kgq = active ? my_kg : 0;
                 const int tok_last = (rb0 + nrb - 1) / hpt;  // sees the most keys
                 const int lim = min(seg_hi, L - p.s_q + tok_last + 1);
                 const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
-                const int n_iter = (nblk + nkg - 1) / nkg;  // same in every wave
-                const int n_kg = nblk > kgq ? (nblk - kgq + nkg - 1) / nkg : 0;
+                const int npair = (nblk + 1) / 2;
+                const int n_iter = (npair + nkg - 1) / nkg;  // same in every wave
+                const int n_kg = npair > kgq ? (npair - kgq + nkg - 1) / nkg : 0;
                 const bool producer = active && my_rbl == 0;
-                const int step = kKeyBlock * nkg;
-                const int kfirst = seg_lo + kKeyBlock * kgq;
-                char *slots = ring + kgq * S * kBlockBytes;
-                if (producer)
-                    for (int s = 0; s < S - 1 && s < n_kg; ++s)
-                        issue_block(slots + s * kBlockBytes, bc, kfirst + s * step, lane);
+                const int pstep = 2 * kKeyBlock * nkg;
+                const int kfirst = seg_lo + 2 * kKeyBlock * kgq;
+                const int key_end = min(vis_end, seg_hi);
+                char *slots = ring + kgq * kPairSlots * kBlockBytes;
+                auto issue_pair = [&](int pi) {
+                    char *dst = slots + (pi & 1) * 2 * kBlockBytes;
+                    issue_block(dst, bc, kfirst + pi * pstep, lane);
+                    issue_block(dst + kBlockBytes, bc, kfirst + pi * pstep + kKeyBlock, lane);
+                };
+                if (producer && n_kg > 0) issue_pair(0);
                 int i = 0;
                 for (;;) {
-                    float sv[4], mx = -INFINITY;
-                    s16x4 va[kOutTiles];
-                    uint32_t v_addr[4] = {0, 0, 0, 0};
+                    float sv[8], mx = -INFINITY;
+                    uint32_t vA[4] = {0, 0, 0, 0}, vB[4] = {0, 0, 0, 0};
                     bool lagged = false;
                     for (; i < n_iter; ++i) {
-                        if (producer) wait_vm_blocks(min(S - 2, n_kg - 1 - i));
-                        __syncthreads();  // block i is in; every wave is done with block i-1
-                        if (producer && i + S - 1 < n_kg)
-                            issue_block(slots + ((i + S - 1) % S) * kBlockBytes, bc,
-                                        kfirst + (i + S - 1) * step, lane);
-                        const int kb = kfirst + i * step;
+                        if (producer) {
+                            if (i + 1 < n_kg) {
+                                issue_pair(i + 1);
+                                wait_vm<2 * kQkSteps>();  // step i landed, step i+1 may fly
+                            } else {
+                                wait_vm<0>();
+                            }
+                        }
+                        bare_barrier();  // step i is in; every wave is done with step i-1
+                        const int kb = kfirst + i * pstep;
                         if (active && i < n_kg && kb < vis_end) {
-                            char *cur = slots + (i % S) * kBlockBytes;
+                            const char *stA = slots + (i & 1) * 2 * kBlockBytes;
+                            const char *stB = stA + kBlockBytes;
 #pragma unroll
-                            for (int c4 = 0; c4 < 4; ++c4)
-                                v_addr[c4] = (uint32_t)(uintptr_t)cur + offs.v_off[c4];
-                            block_scores(sv, mx, va, cur, offs.k_off, v_addr, qf, kb, vis_end,
-                                         p.scale_log2, lane);
+                            for (int c4 = 0; c4 < 4; ++c4) {
+                                vA[c4] = (uint32_t)(uintptr_t)stA + offs.v_off[c4];
+                                vB[c4] = (uint32_t)(uintptr_t)stB + offs.v_off[c4];
+                            }
+                            pair_scores(sv, mx, stA, stB, offs.k_off, qf, kb, kb + kKeyBlock, key_end,
+                                        p.scale_log2, lane);
                             if (__any(mx > ws.m + kMaxLag)) {
                                 lagged = true;
                                 break;
                             }
-                            block_pv(ws, sv, va, v_addr);
+                            pair_pv(ws, sv, vA, vB);
                         }
                         wait_lgkm0();
                     }
                     if (!lagged) break;
                     rescale(ws, mx);
-                    block_pv(ws, sv, va, v_addr);
+                    pair_pv(ws, sv, vA, vB);
                     wait_lgkm0();
                     ++i;
                 }

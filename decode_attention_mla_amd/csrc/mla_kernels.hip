@@ -311,6 +311,42 @@ __device__ inline void read_vt8(s16x4 (&va)[kOutTiles], const uint32_t (&v)[4]) 
         : "memory");
 }
 
+// Eight transposing V^T reads, tiles 2G and 2G+1 of blocks A and B (tile ct
+// at base[ct % 4] + 1024 (ct / 4)), issued without waiting.  The results
+// are only defined after vt_wait4 on the same registers: that statement
+// names them as read-write operands, so the compiler cannot read, copy or
+// reuse them while the loads are in flight.
+template <int G>
+__device__ inline void vt_issue4(s16x4 (&d)[4], const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
+    constexpr int c0 = (2 * G) & 3, c1 = (2 * G + 1) & 3, off = 1024 * ((2 * G) >> 2);
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n"
+        "ds_read_b64_tr_b16 %1, %5 offset:%8\n"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n"
+        "ds_read_b64_tr_b16 %3, %7 offset:%8"
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
+        : "v"(vA[c0]), "v"(vB[c0]), "v"(vA[c1]), "v"(vB[c1]), "n"(off)
+        : "memory");
+}
+
+__device__ inline void vt_wait4(s16x4 (&d)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]) :: "memory");
+}
+
+// Four transposing V^T reads of one block, tiles 4G .. 4G+3, issued without
+// waiting (complete after vt_wait4).
+template <int G>
+__device__ inline void vt_issue_tiles4(s16x4 (&d)[4], const uint32_t (&v)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n"
+        "ds_read_b64_tr_b16 %1, %5 offset:%8\n"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n"
+        "ds_read_b64_tr_b16 %3, %7 offset:%8"
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
+        : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "n"(1024 * G)
+        : "memory");
+}
+
 // Scores of one block: S^T[key][head] for 16 keys x 16 heads, scaled into
 // the log2 domain and masked; lane l holds head l%16, keys kb + 4(l/16) + i
 // and mx is the block max of its head.  The A operand K comes from the
@@ -346,8 +382,8 @@ __device__ inline void block_scores(float (&sv)[4], float &mx, s16x4 (&va)[kOutT
 
 // P = exp2(s - m) and O^T += V^T P^T.  P^T is already in the 16x16x16 B
 // layout (lane: head l%16, keys 4(l/16) + i) and is split into bf16 hi + lo.
-// The other 24 V^T operands are read eight at a time while the MFMAs of
-// the previous eight run.
+// Tiles 0..7 were read with the scores; the others are read four at a time,
+// each group in flight while the MFMAs of the previous four run.
 __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)[kOutTiles],
                                 const uint32_t (&v_addr)[4]) {
     s16x4 phi, plo;
@@ -361,39 +397,31 @@ __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)
         plo[i] = (short)bf16_bits(pr - bf16_value(h));
     }
     st.l += psum;
+    // Group k = tiles 4k .. 4k+3: groups 0 and 1 are in va, group k >= 2 in
+    // buf[k & 1], issued while the MFMAs of group k-1 run.
+    s16x4 buf[2][4];
 #pragma unroll
-    for (int g = 0; g < kOutTiles / 8; ++g) {
-        if (g == 1) read_vt8<1>(va, v_addr);
-        if (g == 2) read_vt8<2>(va, v_addr);
-        if (g == 3) read_vt8<3>(va, v_addr);
-#pragma unroll
-        for (int ct = 8 * g; ct < 8 * g + 8; ++ct) {
-            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], phi, st.acc[ct], 0, 0, 0);
-            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], plo, st.acc[ct], 0, 0, 0);
+    for (int g = 0; g < kOutTiles / 4; ++g) {
+        switch (g + 1) {
+        case 2: vt_issue_tiles4<2>(buf[0], v_addr); break;
+        case 3: vt_issue_tiles4<3>(buf[1], v_addr); break;
+        case 4: vt_issue_tiles4<4>(buf[0], v_addr); break;
+        case 5: vt_issue_tiles4<5>(buf[1], v_addr); break;
+        case 6: vt_issue_tiles4<6>(buf[0], v_addr); break;
+        case 7: vt_issue_tiles4<7>(buf[1], v_addr); break;
+        default: break;
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ct = 4 * g + j;
+            const s16x4 a = g < 2 ? va[ct] : buf[g & 1][j];
+            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, st.acc[ct], 0, 0, 0);
+            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, st.acc[ct], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 >= 2 && g + 1 < kOutTiles / 4) vt_wait4(buf[(g + 1) & 1]);
     }
-}
-
-// Sixteen transposing V^T reads: tiles 4G .. 4G+3 of blocks A and B (bases
-// vA / vB as in read_vt8), waited for inside the statement.
-template <int G>
-__device__ inline void read_vt_pair4(s16x4 (&va)[kOutTiles], s16x4 (&vb)[kOutTiles],
-                                     const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%16\n"
-        "ds_read_b64_tr_b16 %1, %9 offset:%16\n"
-        "ds_read_b64_tr_b16 %2, %10 offset:%16\n"
-        "ds_read_b64_tr_b16 %3, %11 offset:%16\n"
-        "ds_read_b64_tr_b16 %4, %12 offset:%16\n"
-        "ds_read_b64_tr_b16 %5, %13 offset:%16\n"
-        "ds_read_b64_tr_b16 %6, %14 offset:%16\n"
-        "ds_read_b64_tr_b16 %7, %15 offset:%16\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(va[4 * G + 0]), "=&v"(va[4 * G + 1]), "=&v"(va[4 * G + 2]), "=&v"(va[4 * G + 3]),
-          "=&v"(vb[4 * G + 0]), "=&v"(vb[4 * G + 1]), "=&v"(vb[4 * G + 2]), "=&v"(vb[4 * G + 3])
-        : "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "v"(vB[0]), "v"(vB[1]), "v"(vB[2]),
-          "v"(vB[3]), "n"(1024 * G)
-        : "memory");
 }
 
 // ---- 32-key steps (shared rings): two 16-key blocks A and B per step ----
@@ -454,24 +482,45 @@ __device__ inline void pair_pv(WaveState &st, const float (&sv)[8], const uint32
         plo[i] = static_cast<__bf16>(pr - static_cast<float>(h));
     }
     st.l += psum;
-    s16x4 va[kOutTiles], vb[kOutTiles];
+    // Software pipeline over 16 pairs of tiles: the reads of pair g+1 are in
+    // flight while the MFMAs of pair g run.
+    s16x4 buf[2][4];
+    vt_issue4<0>(buf[0], vA, vB);
+    vt_wait4(buf[0]);
 #pragma unroll
-    for (int g = 0; g < kOutTiles / 4; ++g) {
-        if (g == 0) read_vt_pair4<0>(va, vb, vA, vB);
-        if (g == 1) read_vt_pair4<1>(va, vb, vA, vB);
-        if (g == 2) read_vt_pair4<2>(va, vb, vA, vB);
-        if (g == 3) read_vt_pair4<3>(va, vb, vA, vB);
-        if (g == 4) read_vt_pair4<4>(va, vb, vA, vB);
-        if (g == 5) read_vt_pair4<5>(va, vb, vA, vB);
-        if (g == 6) read_vt_pair4<6>(va, vb, vA, vB);
-        if (g == 7) read_vt_pair4<7>(va, vb, vA, vB);
+    for (int g = 0; g < kOutTiles / 2; ++g) {
+        s16x4 (&cur)[4] = buf[g & 1];
+        s16x4 (&nxt)[4] = buf[(g + 1) & 1];
+        switch (g + 1) {  // compile-time after unrolling
+        case 1: vt_issue4<1>(nxt, vA, vB); break;
+        case 2: vt_issue4<2>(nxt, vA, vB); break;
+        case 3: vt_issue4<3>(nxt, vA, vB); break;
+        case 4: vt_issue4<4>(nxt, vA, vB); break;
+        case 5: vt_issue4<5>(nxt, vA, vB); break;
+        case 6: vt_issue4<6>(nxt, vA, vB); break;
+        case 7: vt_issue4<7>(nxt, vA, vB); break;
+        case 8: vt_issue4<8>(nxt, vA, vB); break;
+        case 9: vt_issue4<9>(nxt, vA, vB); break;
+        case 10: vt_issue4<10>(nxt, vA, vB); break;
+        case 11: vt_issue4<11>(nxt, vA, vB); break;
+        case 12: vt_issue4<12>(nxt, vA, vB); break;
+        case 13: vt_issue4<13>(nxt, vA, vB); break;
+        case 14: vt_issue4<14>(nxt, vA, vB); break;
+        case 15: vt_issue4<15>(nxt, vA, vB); break;
+        default: break;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // reads first, then this pair's MFMAs
 #pragma unroll
-        for (int ct = 4 * g; ct < 4 * g + 4; ++ct) {
+        for (int j = 0; j < 2; ++j) {
+            const int ct = 2 * g + j;
             const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(va[ct], vb[ct], 0, 1, 2, 3, 4, 5, 6, 7));
+                bf16x8, __builtin_shufflevector(cur[2 * j], cur[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
             st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[ct], 0, 0, 0);
             st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[ct], 0, 0, 0);
         }
+        // Keep this pair's MFMAs ahead of the wait for the next pair's reads.
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 < kOutTiles / 2) vt_wait4(nxt);
     }
 }
 

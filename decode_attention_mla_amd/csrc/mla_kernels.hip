@@ -169,6 +169,40 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The 18 query chunks of a lane (Q^T operand: channels 32t + 8(l/16) ..+7
+// of row l%16), loaded straight into accumulation registers, from which the
+// MFMA reads its B operand, so the vector registers stay free for the hot
+// loop.  All loads issue back to back and one wait at the end covers them
+// (and any older load of the wave).
+__device__ inline void load_q(bf16x8 (&qf)[kQkSteps], const uint16_t *qrow) {
+    static_assert(kQkSteps == 18, "one load per 32-channel step");
+    asm volatile(
+        "global_load_dwordx4 %0, %18, off\n\t"
+        "global_load_dwordx4 %1, %18, off offset:64\n\t"
+        "global_load_dwordx4 %2, %18, off offset:128\n\t"
+        "global_load_dwordx4 %3, %18, off offset:192\n\t"
+        "global_load_dwordx4 %4, %18, off offset:256\n\t"
+        "global_load_dwordx4 %5, %18, off offset:320\n\t"
+        "global_load_dwordx4 %6, %18, off offset:384\n\t"
+        "global_load_dwordx4 %7, %18, off offset:448\n\t"
+        "global_load_dwordx4 %8, %18, off offset:512\n\t"
+        "global_load_dwordx4 %9, %18, off offset:576\n\t"
+        "global_load_dwordx4 %10, %18, off offset:640\n\t"
+        "global_load_dwordx4 %11, %18, off offset:704\n\t"
+        "global_load_dwordx4 %12, %18, off offset:768\n\t"
+        "global_load_dwordx4 %13, %18, off offset:832\n\t"
+        "global_load_dwordx4 %14, %18, off offset:896\n\t"
+        "global_load_dwordx4 %15, %18, off offset:960\n\t"
+        "global_load_dwordx4 %16, %18, off offset:1024\n\t"
+        "global_load_dwordx4 %17, %18, off offset:1088\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=a"(qf[0]), "=a"(qf[1]), "=a"(qf[2]), "=a"(qf[3]), "=a"(qf[4]), "=a"(qf[5]),
+          "=a"(qf[6]), "=a"(qf[7]), "=a"(qf[8]), "=a"(qf[9]), "=a"(qf[10]), "=a"(qf[11]),
+          "=a"(qf[12]), "=a"(qf[13]), "=a"(qf[14]), "=a"(qf[15]), "=a"(qf[16]), "=a"(qf[17])
+        : "v"(qrow)
+        : "memory");
+}
+
 // ------------------------------------------------------------- per-wave state
 
 struct WaveState {
@@ -195,24 +229,38 @@ struct BlockCtx {
 // 16-byte bank group four times, a V^T read every 8-byte group twice).
 __device__ inline int row_swz(int r) { return 4 * ((r >> 1) & 1) + 2 * ((r >> 2) & 1); }
 
+// Block-table entry of the page that holds key `key` (clamped to the last
+// key, which keeps the index inside the sequence's row), clamped into the
+// pool.  The table is only read by this kernel, so it is read as constant
+// memory through the scalar cache: the load then completes on the
+// LDS/scalar counter and never makes the wave wait for the KV blocks still
+// in flight on the vector-memory counter.  Contiguous caches need no entry.
+__device__ inline int64_t page_of(const BlockCtx &c, int key) {
+    if (!c.page_size) return 0;
+    const int idx = uniform(min(key, c.last_key) / c.page_size);
+    const auto *row = (const __attribute__((address_space(4))) int32_t *)(uintptr_t)uniform(
+        (int64_t)(uintptr_t)c.table_row);
+    const int64_t page = row[idx];
+    return page < 0 ? 0 : (page >= c.num_pages ? c.num_pages - 1 : page);
+}
+
 // Issue the 18 direct-to-LDS 16-byte loads of the block starting at key kb,
 // non-temporal (the cache is streamed once).  Lane l of load t = 9h + u
 // fetches row 8h + l/8, chunk 8u + ((l % 8) ^ swz(l/8)); the hardware stores
-// it at slice t, slot l.
-__device__ inline void issue_block(char *stage, const BlockCtx &c, int kb, int lane) {
+// it at slice t, slot l.  A paged block lies in one page (`page`, from
+// page_of): pages hold a multiple of 16 keys and blocks start at multiples
+// of 16, and a key clamped to the last one stays in the block.
+__device__ inline void issue_block(char *stage, const BlockCtx &c, int kb, int64_t page, int lane) {
     const int r = lane >> 3;
     const int w = (lane & 7) ^ row_swz(r);
     const uint16_t *rows[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int key = min(kb + 8 * h + r, c.last_key);
-        if (c.page_size) {
-            int64_t page = c.table_row[kb / c.page_size];  // one page per 16-key block
-            page = page < 0 ? 0 : (page >= c.num_pages ? c.num_pages - 1 : page);
+        if (c.page_size)
             rows[h] = c.kv + (page * c.page_size + key % c.page_size) * (int64_t)kDqk + 8 * w;
-        } else {
+        else
             rows[h] = c.kv + (c.seq_base + key) * (int64_t)kDqk + 8 * w;
-        }
     }
 #pragma unroll
     for (int t = 0; t < kQkSteps; ++t)
@@ -614,23 +662,9 @@ void mla_split_kernel(Params p) {
             bc.last_key = L - 1;
             const int vis_end = L - p.s_q + tok + 1;  // keys [0, vis_end) visible to this wave
             bf16x8 qf[kQkSteps];  // B operand Q^T: lane l -> head l%16, channels 32t + 8(l/16)
-            if (active) {
-                const uint16_t *qrow =
-                    p.q + (((int64_t)b * p.s_q + tok) * p.heads + h0 + (lane & 15)) * kDqk +
-                    8 * (lane >> 4);
-#pragma unroll
-                for (int t = 0; t < kQkSteps; ++t) {
-                    qf[t] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * t);
-                    // Keep Q^T in accumulation registers (the MFMA reads its B
-                    // operand from there): the vector registers stay free for the
-                    // operand reads of the hot loop.
-                    asm volatile("" : "+a"(qf[t]));
-                }
-            }
-            // No wait here: the query loads (and the previous segment's
-            // stores) are older than every direct load issued below, and the
-            // vector-memory counter drains in order, so each block wait also
-            // covers them.
+            if (active)
+                load_q(qf, p.q + (((int64_t)b * p.s_q + tok) * p.heads + h0 + (lane & 15)) * kDqk +
+                                8 * (lane >> 4));
 
             if (nrb == 1) {
                 // One row block: each wave streams its own blocks (every
@@ -642,7 +676,10 @@ void mla_split_kernel(Params p) {
                 const int kfirst = seg_lo + kKeyBlock * my_kg;
                 char *stage0 = ring + wave * kBlockBytes;
                 char *stage1 = ring + kStageBytes + wave * kBlockBytes;
-                if (n_my > 0) issue_block(stage0, bc, kfirst, lane);
+                // Pages are looked up one block ahead of their issue.
+                int64_t pg = page_of(bc, kfirst);
+                if (n_my > 0) issue_block(stage0, bc, kfirst, pg, lane);
+                pg = page_of(bc, kfirst + step);
                 int i = 0;
                 for (;;) {
                     float sv[4], mx = -INFINITY;
@@ -652,7 +689,8 @@ void mla_split_kernel(Params p) {
                     for (; i < n_my; ++i) {
                         char *cur = (i & 1) ? stage1 : stage0;
                         if (i + 1 < n_my) {
-                            issue_block((i & 1) ? stage0 : stage1, bc, kfirst + (i + 1) * step, lane);
+                            issue_block((i & 1) ? stage0 : stage1, bc, kfirst + (i + 1) * step, pg, lane);
+                            pg = page_of(bc, kfirst + (i + 2) * step);
                             wait_vm<kQkSteps>();  // block i landed, block i+1 may fly
                         } else {
                             wait_vm<0>();
@@ -693,10 +731,15 @@ void mla_split_kernel(Params p) {
                 const int kfirst = seg_lo + 2 * kKeyBlock * kgq;
                 const int key_end = min(vis_end, seg_hi);
                 char *slots = ring + kgq * kPairSlots * kBlockBytes;
+                // Pages are looked up one step ahead of their issue.
+                int64_t pgA = page_of(bc, kfirst), pgB = page_of(bc, kfirst + kKeyBlock);
                 auto issue_pair = [&](int pi) {
                     char *dst = slots + (pi & 1) * 2 * kBlockBytes;
-                    issue_block(dst, bc, kfirst + pi * pstep, lane);
-                    issue_block(dst + kBlockBytes, bc, kfirst + pi * pstep + kKeyBlock, lane);
+                    const int kb = kfirst + pi * pstep;
+                    issue_block(dst, bc, kb, pgA, lane);
+                    issue_block(dst + kBlockBytes, bc, kb + kKeyBlock, pgB, lane);
+                    pgA = page_of(bc, kb + pstep);
+                    pgB = page_of(bc, kb + pstep + kKeyBlock);
                 };
                 if (producer && n_kg > 0) issue_pair(0);
                 int i = 0;

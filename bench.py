@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark: MLA decode attention on one MI355X.
 
-One step = one mla_decode call (split plan + split kernel + combine kernel)
-over the whole batch, inputs already resident in HBM.  The default workload
+One step = one mla_decode call (split kernel: plan and attention over each
+key range; combine kernel: merge of the sequences split across ranges) over
+the whole batch, inputs already resident in HBM.  The default workload
 is batch 16, 16 heads, one query token, 65536 cached keys per sequence
 (KV cache 1,207,959,552 B, larger than the 256 MB last-level cache, so every
 step streams it from HBM).  Prints one JSON line.
@@ -93,6 +94,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--splits", type=int, default=0, help="key ranges per launch (0: library default)")
+    ap.add_argument("--min-chunk", type=int, default=0, help="smallest key range (0: library default)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -126,6 +129,8 @@ def main() -> int:
     out = torch.empty((w.batch, w.s_q, w.heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.batch, w.s_q, w.heads), dtype=torch.float32, device="cuda")
     ctx = mla.Context()
+    ctx.set_option(mla.MLA_OPT_NUM_SPLITS, args.splits)
+    ctx.set_option(mla.MLA_OPT_MIN_CHUNK, args.min_chunk)
     ctx.reserve(w.s_q, w.heads)
 
     def step(i):
@@ -177,7 +182,8 @@ def main() -> int:
         "config": {"workload": name, "batch": w.batch, "s_q": w.s_q, "heads": w.heads,
                    "kv_len": w.seqlen if isinstance(w.seqlen, int) else list(w.seqlen),
                    "layout": "paged%d" % w.page_size if w.page_size else "contiguous",
-                   "kv_bytes": kv_bytes, "cache_copies_rotated": len(copies)},
+                   "kv_bytes": kv_bytes, "cache_copies_rotated": len(copies),
+                   "splits": args.splits or "default", "min_chunk": args.min_chunk or "default"},
         "roofline": {
             "bound": "hbm",
             "kernel": "mla_split_kernel",

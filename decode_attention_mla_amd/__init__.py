@@ -119,7 +119,7 @@ def make_problem(batch, s_q, num_heads, page_size=0, kv_capacity=0, num_pages=0,
     return pr, keep
 
 
-def mla_plan(seqlens: Sequence[int], num_splits: int, min_chunk: int = 256):
+def mla_plan(seqlens: Sequence[int], num_splits: int, min_chunk: int = 64):
     """Host mirror of the device split plan: (segments as dicts, info dict)."""
     lib = load()
     lens = np.ascontiguousarray(seqlens, dtype=np.int32)

@@ -151,6 +151,24 @@ __device__ inline int64_t plan_total(const Params &p, int lane) {
     return uniform(total);
 }
 
+// Where sequence b lies on the line of padded keys: its start, its padded
+// length, and the total over all sequences (every lane gets all three).
+// One length load per lane per 64 sequences, all issued before any sum.
+__device__ inline void line_position(const Params &p, int b, int lane, int64_t &total,
+                                     int64_t &start, int64_t &len) {
+    int64_t t = 0, s = 0, l = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int bl = b0 + lane;
+        const int64_t lpl = bl < p.batch ? padded_len(seq_len(p, bl)) : 0;
+        t += lpl;
+        s += bl < b ? lpl : 0;
+        l += bl == b ? lpl : 0;
+    }
+    total = uniform(wave_sum_i64(t));
+    start = uniform(wave_sum_i64(s));
+    len = uniform(wave_sum_i64(l));
+}
+
 __device__ inline uint16_t bf16_bits(float x) {
     __bf16 h = static_cast<__bf16>(x);
     return __builtin_bit_cast(uint16_t, h);
@@ -661,25 +679,49 @@ void mla_split_kernel(Params p) {
             bc.seq_base = (int64_t)b * p.kv_capacity;
             bc.last_key = L - 1;
             const int vis_end = L - p.s_q + tok + 1;  // keys [0, vis_end) visible to this wave
+            // This wave's keys.  One row block: every nkg-th 16-key block
+            // from kfirst.  Several: the waves of a key group (same keys,
+            // different row blocks) share each 32-key step, two 16-key
+            // blocks, and the group takes every nkg-th step from kfirst.
+            const int kgq = active ? my_kg : 0;
+            const bool producer = active && my_rbl == 0;  // loads the keys of its group
+            int kfirst, kstep, n_mine, n_iter = 0;
+            if (nrb == 1) {
+                const int lim = min(seg_hi, vis_end);
+                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
+                n_mine = nblk > my_kg ? (nblk - my_kg + nkg - 1) / nkg : 0;
+                kstep = kKeyBlock * nkg;
+                kfirst = seg_lo + kKeyBlock * my_kg;
+            } else {
+                const int tok_last = (rb0 + nrb - 1) / hpt;  // sees the most keys
+                const int lim = min(seg_hi, L - p.s_q + tok_last + 1);
+                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
+                const int npair = (nblk + 1) / 2;
+                n_iter = (npair + nkg - 1) / nkg;  // same in every wave
+                n_mine = npair > kgq ? (npair - kgq + nkg - 1) / nkg : 0;
+                kstep = 2 * kKeyBlock * nkg;
+                kfirst = seg_lo + 2 * kKeyBlock * kgq;
+            }
+            // The first loads of the segment go out before the query is
+            // fetched, so that the two round trips overlap.
+            char *const first = ring + (nrb == 1 ? wave : kgq * kPairSlots) * kBlockBytes;
+            if (producer && n_mine > 0) {
+                issue_block(first, bc, kfirst, page_of(bc, kfirst), lane);
+                if (nrb > 1) issue_block(first + kBlockBytes, bc, kfirst + kKeyBlock,
+                                         page_of(bc, kfirst + kKeyBlock), lane);
+            }
             bf16x8 qf[kQkSteps];  // B operand Q^T: lane l -> head l%16, channels 32t + 8(l/16)
             if (active)
                 load_q(qf, p.q + (((int64_t)b * p.s_q + tok) * p.heads + h0 + (lane & 15)) * kDqk +
                                 8 * (lane >> 4));
 
             if (nrb == 1) {
-                // One row block: each wave streams its own blocks (every
-                // kWaves-th one) through a private two-stage ring, no barrier.
-                const int lim = min(seg_hi, vis_end);
-                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
-                const int n_my = nblk > my_kg ? (nblk - my_kg + nkg - 1) / nkg : 0;
-                const int step = kKeyBlock * nkg;
-                const int kfirst = seg_lo + kKeyBlock * my_kg;
-                char *stage0 = ring + wave * kBlockBytes;
-                char *stage1 = ring + kStageBytes + wave * kBlockBytes;
-                // Pages are looked up one block ahead of their issue.
-                int64_t pg = page_of(bc, kfirst);
-                if (n_my > 0) issue_block(stage0, bc, kfirst, pg, lane);
-                pg = page_of(bc, kfirst + step);
+                // One row block: each wave streams its own blocks through a
+                // private two-stage ring, no barrier.
+                const int n_my = n_mine, step = kstep;
+                char *stage0 = first;
+                char *stage1 = first + kStageBytes;
+                int64_t pg = page_of(bc, kfirst + step);  // pages are looked up a block ahead
                 int i = 0;
                 for (;;) {
                     float sv[4], mx = -INFINITY;
@@ -714,25 +756,14 @@ void mla_split_kernel(Params p) {
                     ++i;
                 }
             } else {
-                // Several row blocks: the waves of a key group (same keys,
-                // different row blocks) share each 32-key step, two 16-key
-                // blocks.  One producer wave per key group loads it into a
-                // shared ring of two steps; a barrier per step publishes it
-                // and frees the slots read one step ago.
-                const int kgq = active ? my_kg : 0;
-                const int tok_last = (rb0 + nrb - 1) / hpt;  // sees the most keys
-                const int lim = min(seg_hi, L - p.s_q + tok_last + 1);
-                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
-                const int npair = (nblk + 1) / 2;
-                const int n_iter = (npair + nkg - 1) / nkg;  // same in every wave
-                const int n_kg = npair > kgq ? (npair - kgq + nkg - 1) / nkg : 0;
-                const bool producer = active && my_rbl == 0;
-                const int pstep = 2 * kKeyBlock * nkg;
-                const int kfirst = seg_lo + 2 * kKeyBlock * kgq;
+                // Several row blocks: the producer wave of each key group
+                // loads its steps into a shared ring of two; a barrier per
+                // step publishes it and frees the slots read one step ago.
+                const int n_kg = n_mine, pstep = kstep;
                 const int key_end = min(vis_end, seg_hi);
-                char *slots = ring + kgq * kPairSlots * kBlockBytes;
+                char *slots = first;
                 // Pages are looked up one step ahead of their issue.
-                int64_t pgA = page_of(bc, kfirst), pgB = page_of(bc, kfirst + kKeyBlock);
+                int64_t pgA = page_of(bc, kfirst + pstep), pgB = page_of(bc, kfirst + pstep + kKeyBlock);
                 auto issue_pair = [&](int pi) {
                     char *dst = slots + (pi & 1) * 2 * kBlockBytes;
                     const int kb = kfirst + pi * pstep;
@@ -741,7 +772,6 @@ void mla_split_kernel(Params p) {
                     pgA = page_of(bc, kb + pstep);
                     pgB = page_of(bc, kb + pstep + kKeyBlock);
                 };
-                if (producer && n_kg > 0) issue_pair(0);
                 int i = 0;
                 for (;;) {
                     float sv[8], mx = -INFINITY;
@@ -865,15 +895,9 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
     const int head = threadIdx.x >> 4;
     const int c = blockIdx.z * kCombineChannels + 4 * (threadIdx.x & 15);
 
-    const int64_t total = plan_total(p, lane);
+    int64_t total, st_b, lp;
+    line_position(p, b, lane, total, st_b, lp);
     const int64_t chunk = plan_chunk(total, p.splits, p.min_chunk);
-    int64_t st_b = 0;
-    for (int b0 = 0; b0 < b; b0 += 64) {
-        const int bl = b0 + lane;
-        st_b += wave_sum_i64(bl < b ? padded_len(seq_len(p, bl)) : 0);
-    }
-    st_b = uniform(st_b);
-    const int64_t lp = padded_len(seq_len(p, b));
     const int hpt = p.heads >> 4;
     const int t = rb / hpt;
     const int hh = (rb % hpt) * 16 + head;
@@ -937,7 +961,7 @@ struct mla_ctx {
     int device = 0;
     int cu_count = 256;
     int64_t opt_splits = 0;
-    int64_t opt_min_chunk = 256;
+    int64_t opt_min_chunk = mla::kDefaultMinChunk;
     bool timing = false;
     void *ws = nullptr;
     size_t ws_bytes = 0;
@@ -1024,7 +1048,7 @@ int check(mla_ctx *ctx, const void *q, const void *kv, const int32_t *block_tabl
     return MLA_OK;
 }
 
-int64_t min_chunk_of(const mla_ctx *ctx) { return ctx->opt_min_chunk > 0 ? ctx->opt_min_chunk : 256; }
+int64_t min_chunk_of(const mla_ctx *ctx) { return ctx->opt_min_chunk > 0 ? ctx->opt_min_chunk : mla::kDefaultMinChunk; }
 
 }  // namespace
 
@@ -1129,7 +1153,7 @@ int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value) {
         return MLA_OK;
     case MLA_OPT_MIN_CHUNK:
         if (value < 0 || value > ((int64_t)1 << 31)) return fail(ctx, MLA_ERR_INVALID_ARG, "bad min chunk");
-        ctx->opt_min_chunk = value ? value : 256;
+        ctx->opt_min_chunk = value ? value : mla::kDefaultMinChunk;
         return MLA_OK;
     case MLA_OPT_KERNEL_TIMING:
         ctx->timing = value != 0;

@@ -19,6 +19,10 @@ namespace mla {
 
 constexpr int kKeyBlock = 16;   // keys per wave block
 constexpr int kChunkAlign = kKeyBlock;  // range sizes are multiples of this
+// Default smallest range: one 16-key block for each of a workgroup's four
+// waves.  Small problems then spread over more workgroups (their time is
+// round trips, not bytes); large ones never reach it.
+constexpr int64_t kDefaultMinChunk = 64;
 
 __host__ __device__ inline int64_t padded_len(int64_t len) {
     return (len + kKeyBlock - 1) / kKeyBlock * kKeyBlock;

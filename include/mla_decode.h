@@ -108,7 +108,7 @@ int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads);
  *  MLA_OPT_NUM_SPLITS  number of key-range workgroups per row-block group
  *                      (default: the device's CU count); 0 restores it.
  *  MLA_OPT_MIN_CHUNK   smallest key range given to one workgroup (default
- *                      256, rounded up to MLA_KEY_BLOCK).
+ *                      64, rounded up to MLA_KEY_BLOCK); 0 restores it.
  *  MLA_OPT_KERNEL_TIMING  1: bracket every kernel launch with HIP events on
  *                      the context's stream (see mla_ctx_kernel_times); 0: off.
  */

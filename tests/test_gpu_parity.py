@@ -83,6 +83,51 @@ def test_small_shapes_against_oracle(ctx, case, splits, min_chunk):
         ctx.set_option(mla.MLA_OPT_MIN_CHUNK, 0)
 
 
+# Device lengths outside [s_q, capacity] (the host does not see them): the
+# kernels clamp them to [0, capacity], and a row whose causal window
+# [0, L - s_q + t] holds no key is defined as O = 0, LSE = -inf.  The other
+# rows are single-token attentions over the window, which the oracle gives.
+OUT_OF_CONTRACT = [
+    # (B, s_q, H, device lens, page_size, capacity)
+    (4, 1, 16, [0, 5, 0, 40], 0, 48),
+    (3, 4, 16, [0, 2, 300], 16, 320),
+    (2, 4, 32, [1, 3], 64, 64),
+    (3, 2, 16, [0, 0, 0], 0, 16),
+    (2, 2, 16, [40, 1000], 0, 33),   # longer than the cache: clamped to 33
+]
+
+
+@pytest.mark.parametrize("case", range(len(OUT_OF_CONTRACT)))
+def test_device_lengths_outside_the_contract(ctx, case):
+    import torch
+
+    B, s_q, H, lens, ps, cap = OUT_OF_CONTRACT[case]
+    announce(f"device lengths {OUT_OF_CONTRACT[case]}")
+    held = [min(n, cap) for n in lens]
+    w = wl.Workload("e", B, s_q, H, max(max(held), 1), ps, 200 + case)
+    inp = wl.make_inputs(w, poison=True, seqlens=held, capacity=cap)
+    dev = list(to_device(inp))
+    dev[3] = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    # outputs start as NaN: every row must be written
+    out = torch.full((B, s_q, H, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, s_q, H), float("nan"), dtype=torch.float32, device="cuda")
+    o, l = run_gpu(ctx, inp, dev=dev, host_lens=False, out=out, lse=lse)
+    n_empty = 0
+    for b in range(B):
+        for t in range(s_q):
+            vis = held[b] - s_q + t + 1
+            if vis <= 0:
+                n_empty += 1
+                assert np.all(np.isneginf(l[b, t])) and np.all(o[b, t] == 0.0), (b, t)
+                continue
+            bt = None if inp.block_table is None else inp.block_table[b:b + 1]
+            kv = inp.kv if inp.block_table is not None else inp.kv[b:b + 1]
+            ro, rl = oracle.mla_decode(inp.q[b:b + 1, t:t + 1], kv, bt,
+                                       np.array([vis], np.int32), inp.scale)
+            compare(o[b:b + 1, t:t + 1], l[b:b + 1, t:t + 1], ro, rl, f"{OUT_OF_CONTRACT[case]} b={b} t={t}")
+    assert n_empty > 0 or case == len(OUT_OF_CONTRACT) - 1
+
+
 def test_single_key_returns_value_row_exactly(ctx):
     announce("single key")
     inp = wl.small("one", 4, 1, 16, [1, 1, 1, 1], page_size=64, seed=5)

@@ -93,6 +93,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed steps for this long before the warmup steps (clock ramp)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="key ranges per launch (0: library default)")
     ap.add_argument("--min-chunk", type=int, default=0, help="smallest key range (0: library default)")
@@ -137,7 +139,17 @@ def main() -> int:
         mla.mla_decode(ctx, q, copies[i % len(copies)], bt, lens, inp.scale, out=out, lse=lse,
                        seqlens_host=inp.seqlens)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    # The GPU's clocks reach their steady state only after some milliseconds
+    # of load (input generation leaves it idle for seconds).  Untimed steps
+    # run for --settle-s seconds first, then the W warmup steps, so that the
+    # K timed steps see the clocks a serving loop runs at.
+    settle_steps, s0 = 0, time.perf_counter()
+    while time.perf_counter() - s0 < args.settle_s:
+        for i in range(10):
+            step(i)
+        torch.cuda.synchronize()
+        settle_steps += 10
+    print(f"[bench] settle {settle_steps} steps, warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -171,6 +183,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_call": round(ms_per_step * 1e3, 2),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),

@@ -927,6 +927,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
             lv[k] = p.part_lse[r];
             ov[k] = *reinterpret_cast<const f32x4 *>(p.part_o + r * kDv + c);
         }
+        __builtin_amdgcn_sched_barrier(0);  // all loads of the batch are in flight before any use
         float mb = -INFINITY;
 #pragma unroll
         for (int k = 0; k < kCombineBatch; ++k) {
@@ -934,13 +935,16 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
             mb = fmaxf(mb, lv[k]);
         }
         const float m_new = fmaxf(M, mb);
-        if (m_new == -INFINITY) continue;  // no key in any part so far
-        const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+        // Until some part holds a key every weight is 0; a finite reference
+        // then keeps exp2 away from -inf - -inf.  (No branch here: a branch
+        // on the LSEs would let the compiler sink the O loads below it.)
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(M - m_ref);
         lsum *= alpha;
         o *= alpha;
 #pragma unroll
         for (int k = 0; k < kCombineBatch; ++k) {
-            const float w = __builtin_amdgcn_exp2f(lv[k] - m_new);  // 0 for -inf parts
+            const float w = __builtin_amdgcn_exp2f(lv[k] - m_ref);  // 0 for -inf parts
             lsum += w;
             o += w * ov[k];
         }

@@ -80,6 +80,7 @@ constexpr int kNonTemporal = 2;                // cache-policy bits of a streami
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 struct Params {
@@ -446,22 +447,28 @@ __device__ inline void block_scores(float (&sv)[4], float &mx, s16x4 (&va)[kOutT
     mx = fmaxf(mx, __shfl_xor(mx, 32));
 }
 
-// P = exp2(s - m) and O^T += V^T P^T.  P^T is already in the 16x16x16 B
-// layout (lane: head l%16, keys 4(l/16) + i) and is split into bf16 hi + lo.
+// P = exp2(s - m) and O^T += V^T P^T, P split into bf16 hi + lo, one
+// 16x16x32 MFMA per output tile for both halves.  Its k index runs over
+// (key, half): lane group g = l/16 holds k = 8g + j, which stands for key
+// 4g + j%4, hi half for j < 4 and lo half for j >= 4.  The B operand is then
+// the lane's own P^T values (head l%16, keys 4g + i: the score accumulator
+// layout) as {hi[0..3], lo[0..3]}, and the A operand the lane's transposed
+// V^T read (channel l%16, keys 4g + i) twice: sum_k A B = V^T (P_hi + P_lo).
 // Tiles 0..7 were read with the scores; the others are read four at a time,
 // each group in flight while the MFMAs of the previous four run.
 __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)[kOutTiles],
                                 const uint32_t (&v_addr)[4]) {
-    s16x4 phi, plo;
+    s16x8 pb;
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float pr = __builtin_amdgcn_exp2f(sv[i] - st.m);
         psum += pr;
         const uint16_t h = bf16_bits(pr);
-        phi[i] = (short)h;
-        plo[i] = (short)bf16_bits(pr - bf16_value(h));
+        pb[i] = (short)h;
+        pb[4 + i] = (short)bf16_bits(pr - bf16_value(h));
     }
+    const bf16x8 p8 = __builtin_bit_cast(bf16x8, pb);
     st.l += psum;
     // Group k = tiles 4k .. 4k+3: groups 0 and 1 are in va, group k >= 2 in
     // buf[k & 1], issued while the MFMAs of group k-1 run.
@@ -482,8 +489,8 @@ __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)
         for (int j = 0; j < 4; ++j) {
             const int ct = 4 * g + j;
             const s16x4 a = g < 2 ? va[ct] : buf[g & 1][j];
-            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, st.acc[ct], 0, 0, 0);
-            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, st.acc[ct], 0, 0, 0);
+            const bf16x8 a8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3));
+            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, p8, st.acc[ct], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (g + 1 >= 2 && g + 1 < kOutTiles / 4) vt_wait4(buf[(g + 1) & 1]);

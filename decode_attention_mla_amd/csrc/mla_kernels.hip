@@ -396,8 +396,27 @@ __device__ inline void vt_issue4(s16x4 (&d)[4], const uint32_t (&vA)[4], const u
         : "memory");
 }
 
+// Tiles 4Q .. 4Q+3 of blocks A and B (eight reads), issued without waiting:
+// d[2j], d[2j+1] are tile 4Q+j of A and B.  Complete after vt_wait8.
+template <int Q>
+__device__ inline void vt_issue_group(s16x4 (&d)[8], const uint32_t (&vA)[4], const uint32_t (&vB)[4]);
+
+__device__ inline void vt_wait8(s16x4 (&d)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]),
+                   "+v"(d[7])
+                 :
+                 : "memory");
+}
+
 __device__ inline void vt_wait4(s16x4 (&d)[4]) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]) :: "memory");
+}
+
+template <int Q>
+__device__ inline void vt_issue_group(s16x4 (&d)[8], const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
+    vt_issue4<2 * Q>(*reinterpret_cast<s16x4(*)[4]>(&d[0]), vA, vB);
+    vt_issue4<2 * Q + 1>(*reinterpret_cast<s16x4(*)[4]>(&d[4]), vA, vB);
 }
 
 // Four transposing V^T reads of one block, tiles 4G .. 4G+3, issued without
@@ -555,45 +574,38 @@ __device__ inline void pair_pv(WaveState &st, const float (&sv)[8], const uint32
         plo[i] = static_cast<__bf16>(pr - static_cast<float>(h));
     }
     st.l += psum;
-    // Software pipeline over 16 pairs of tiles: the reads of pair g+1 are in
-    // flight while the MFMAs of pair g run.
-    s16x4 buf[2][4];
-    vt_issue4<0>(buf[0], vA, vB);
-    vt_wait4(buf[0]);
+    // Software pipeline over 8 groups of 4 tiles: the 8 reads of group q+1
+    // are in flight while the 8 MFMAs of group q run (long enough to cover
+    // an LDS round trip, which a pair of tiles was not).
+    s16x4 buf[2][8];
+    vt_issue_group<0>(buf[0], vA, vB);
+    vt_wait8(buf[0]);
 #pragma unroll
-    for (int g = 0; g < kOutTiles / 2; ++g) {
-        s16x4 (&cur)[4] = buf[g & 1];
-        s16x4 (&nxt)[4] = buf[(g + 1) & 1];
-        switch (g + 1) {  // compile-time after unrolling
-        case 1: vt_issue4<1>(nxt, vA, vB); break;
-        case 2: vt_issue4<2>(nxt, vA, vB); break;
-        case 3: vt_issue4<3>(nxt, vA, vB); break;
-        case 4: vt_issue4<4>(nxt, vA, vB); break;
-        case 5: vt_issue4<5>(nxt, vA, vB); break;
-        case 6: vt_issue4<6>(nxt, vA, vB); break;
-        case 7: vt_issue4<7>(nxt, vA, vB); break;
-        case 8: vt_issue4<8>(nxt, vA, vB); break;
-        case 9: vt_issue4<9>(nxt, vA, vB); break;
-        case 10: vt_issue4<10>(nxt, vA, vB); break;
-        case 11: vt_issue4<11>(nxt, vA, vB); break;
-        case 12: vt_issue4<12>(nxt, vA, vB); break;
-        case 13: vt_issue4<13>(nxt, vA, vB); break;
-        case 14: vt_issue4<14>(nxt, vA, vB); break;
-        case 15: vt_issue4<15>(nxt, vA, vB); break;
+    for (int q = 0; q < kOutTiles / 4; ++q) {
+        s16x4 (&cur)[8] = buf[q & 1];
+        s16x4 (&nxt)[8] = buf[(q + 1) & 1];
+        switch (q + 1) {  // compile-time after unrolling
+        case 1: vt_issue_group<1>(nxt, vA, vB); break;
+        case 2: vt_issue_group<2>(nxt, vA, vB); break;
+        case 3: vt_issue_group<3>(nxt, vA, vB); break;
+        case 4: vt_issue_group<4>(nxt, vA, vB); break;
+        case 5: vt_issue_group<5>(nxt, vA, vB); break;
+        case 6: vt_issue_group<6>(nxt, vA, vB); break;
+        case 7: vt_issue_group<7>(nxt, vA, vB); break;
         default: break;
         }
-        __builtin_amdgcn_sched_barrier(0);  // reads first, then this pair's MFMAs
+        __builtin_amdgcn_sched_barrier(0);  // reads first, then this group's MFMAs
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int ct = 2 * g + j;
+        for (int j = 0; j < 4; ++j) {
+            const int ct = 4 * q + j;
             const bf16x8 a = __builtin_bit_cast(
                 bf16x8, __builtin_shufflevector(cur[2 * j], cur[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
             st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[ct], 0, 0, 0);
             st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[ct], 0, 0, 0);
         }
-        // Keep this pair's MFMAs ahead of the wait for the next pair's reads.
+        // Keep this group's MFMAs ahead of the wait for the next group's reads.
         __builtin_amdgcn_sched_barrier(0);
-        if (g + 1 < kOutTiles / 2) vt_wait4(nxt);
+        if (q + 1 < kOutTiles / 4) vt_wait8(nxt);
     }
 }
 

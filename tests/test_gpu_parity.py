@@ -128,6 +128,31 @@ def test_device_lengths_outside_the_contract(ctx, case):
     assert n_empty > 0 or case == len(OUT_OF_CONTRACT) - 1
 
 
+# Medium decode shapes: many heads (several row-block groups), several
+# query tokens, other page sizes, one long sequence; every row checked.
+MEDIUM = [
+    # (B, s_q, H, lens, page_size)
+    (4, 1, 128, [3000, 1, 777, 4096], 64),
+    (2, 2, 64, [5000, 300], 32),
+    (3, 1, 16, [10000, 20000, 5], 128),
+    (2, 3, 32, [4096, 4097], 256),
+    (1, 4, 16, [65536], 0),
+    (5, 1, 32, [1, 2, 3, 4, 5], 16),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MEDIUM)))
+def test_medium_shapes_against_oracle(ctx, case):
+    B, s_q, H, lens, ps = MEDIUM[case]
+    announce(f"medium {MEDIUM[case]}")
+    inp = wl.small("m", B, s_q, H, lens, page_size=ps, seed=300 + case)
+    o, l = run_gpu(ctx, inp)
+    ro, rl = oracle_of(inp)
+    compare(o, l, ro, rl, str(MEDIUM[case]))
+    o2, l2 = run_gpu(ctx, inp, host_lens=False)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
 def test_single_key_returns_value_row_exactly(ctx):
     announce("single key")
     inp = wl.small("one", 4, 1, 16, [1, 1, 1, 1], page_size=64, seed=5)

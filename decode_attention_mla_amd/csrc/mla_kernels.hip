@@ -625,6 +625,68 @@ __device__ inline void rescale(WaveState &ws, float mx) {
 // the same softmax; the rescale sits outside the hot loop.
 constexpr float kMaxLag = 8.0f;
 
+// ------------------------------------------------- merging a segment's waves
+
+// After a segment the ring holds the waves' O rows for the merge: waves 0
+// and 1 in the first stage, waves 2 and 3 (and the stats) in the second.
+__device__ inline float *merge_row_at(char *ring, int w, int head) {
+    return reinterpret_cast<float *>(ring + (w < 2 ? 0 : kStageBytes)) + ((w & 1) * 16 + head) * kMergePitch;
+}
+
+// Rows of row block rb0 + rbl from the NKG waves that computed them (waves
+// rbl + nrb kg): the LSE-weighted sum of their O rows, normalized, written
+// as the final rows (whole) or as the segment's part.  Every LDS read is
+// issued before the first is used.  256 threads: 16 heads x 16 quads.
+template <int NKG>
+__device__ inline void merge_waves(const Params &p, char *ring, const float *merge_m, const float *merge_l,
+                                   int b, int rb0, int rbl, int nrb, bool whole, int slot) {
+    const int head = threadIdx.x >> 4;
+    const int cq = threadIdx.x & 15;
+    float mw[NKG], lw[NKG];
+    f32x4 ov[kDv / 64][NKG];
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) {
+        const int w = rbl + nrb * kg;
+        mw[kg] = merge_m[w * 16 + head];
+        lw[kg] = merge_l[w * 16 + head];
+#pragma unroll
+        for (int jc = 0; jc < kDv / 64; ++jc)
+            ov[jc][kg] = *reinterpret_cast<const f32x4 *>(merge_row_at(ring, w, head) + 4 * cq + 64 * jc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float M = mw[0];
+#pragma unroll
+    for (int kg = 1; kg < NKG; ++kg) M = fmaxf(M, mw[kg]);
+    float wgt[NKG];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) {
+        wgt[kg] = mw[kg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[kg] - M);
+        lsum += wgt[kg] * lw[kg];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float lse2 = lsum > 0.f ? M + log2f(lsum) : -INFINITY;
+    const int rbg = rb0 + rbl;
+    const int hpt = p.heads >> 4;
+    const int64_t row = ((int64_t)b * p.s_q + rbg / hpt) * p.heads + (rbg % hpt) * 16 + head;
+    float *orow;
+    if (whole) {
+        orow = p.out + row * kDv;
+        if (cq == 0) p.lse[row] = lse2 * kLn2;
+    } else {
+        const int64_t r = ((int64_t)slot * p.n_rb + rbg) * 16 + head;
+        orow = p.part_o + r * kDv;
+        if (cq == 0) p.part_lse[r] = lse2;
+    }
+#pragma unroll
+    for (int jc = 0; jc < kDv / 64; ++jc) {
+        f32x4 o = wgt[0] * ov[jc][0];
+#pragma unroll
+        for (int kg = 1; kg < NKG; ++kg) o += wgt[kg] * ov[jc][kg];
+        *reinterpret_cast<f32x4 *>(orow + 4 * cq + 64 * jc) = o * inv;
+    }
+}
+
 // --------------------------------------------------------------- split kernel
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -653,12 +715,7 @@ void mla_split_kernel(Params p) {
     const int64_t ge = min(gs + chunk, total);
 
     const OperandOffsets offs = operand_offsets(lane);
-    // After a segment the ring holds the waves' O rows for the merge: waves
-    // 0 and 1 in the first stage, waves 2 and 3 (and the stats) in the second.
-    auto merge_row = [&](int w, int head) {
-        return reinterpret_cast<float *>(ring + (w < 2 ? 0 : kStageBytes)) +
-               ((w & 1) * 16 + head) * kMergePitch;
-    };
+    // The waves' merge stats sit after the O rows of waves 2 and 3.
     float *merge_m = reinterpret_cast<float *>(ring + kStageBytes) + 2 * kMergeWaveFloats;
     float *merge_l = merge_m + kWaves * 16;
 
@@ -841,7 +898,7 @@ void mla_split_kernel(Params p) {
                 float lt = ws.l;
                 lt += __shfl_xor(lt, 16);
                 lt += __shfl_xor(lt, 32);
-                float *dst = merge_row(wave, head) + 4 * grp;
+                float *dst = merge_row_at(ring, wave, head) + 4 * grp;
 #pragma unroll
                 for (int ct = 0; ct < kOutTiles; ++ct)
                     *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct];
@@ -851,52 +908,13 @@ void mla_split_kernel(Params p) {
                 }
             }
             __syncthreads();
-            {
-                const int head = threadIdx.x >> 4;
-                const int cq = threadIdx.x & 15;
-                for (int rbl = 0; rbl < nrb; ++rbl) {
-                    float M = -INFINITY;
-                    for (int kg = 0; kg < nkg; ++kg) M = fmaxf(M, merge_m[(rbl + nrb * kg) * 16 + head]);
-                    float wgt[kWaves];
-                    float lsum = 0.f;
-#pragma unroll
-                    for (int kg = 0; kg < kWaves; ++kg) {
-                        wgt[kg] = 0.f;
-                        if (kg < nkg) {
-                            const int w = rbl + nrb * kg;
-                            const float mw = merge_m[w * 16 + head];
-                            wgt[kg] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-                            lsum += wgt[kg] * merge_l[w * 16 + head];
-                        }
-                    }
-                    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-                    const float lse2 = lsum > 0.f ? M + log2f(lsum) : -INFINITY;
-                    const int rbg = rb0 + rbl;
-                    const int t = rbg / hpt;
-                    const int hh = (rbg % hpt) * 16 + head;
-                    float *orow;
-                    if (whole) {
-                        orow = p.out + (((int64_t)b * p.s_q + t) * p.heads + hh) * kDv;
-                        if (cq == 0) p.lse[((int64_t)b * p.s_q + t) * p.heads + hh] = lse2 * kLn2;
-                    } else {
-                        const int64_t r = ((int64_t)slot * p.n_rb + rbg) * 16 + head;
-                        orow = p.part_o + r * kDv;
-                        if (cq == 0) p.part_lse[r] = lse2;
-                    }
-#pragma unroll
-                    for (int jc = 0; jc < kDv / 64; ++jc) {
-                        const int c = 4 * cq + 64 * jc;
-                        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kg = 0; kg < kWaves; ++kg) {
-                            if (kg < nkg) {
-                                const int w = rbl + nrb * kg;
-                                o += wgt[kg] * *reinterpret_cast<const f32x4 *>(merge_row(w, head) + c);
-                            }
-                        }
-                        *reinterpret_cast<f32x4 *>(orow + c) = o * inv;
-                    }
-                }
+            for (int rbl = 0; rbl < nrb; ++rbl) {
+                if (nkg == 4)
+                    merge_waves<4>(p, ring, merge_m, merge_l, b, rb0, rbl, nrb, whole, slot);
+                else if (nkg == 2)
+                    merge_waves<2>(p, ring, merge_m, merge_l, b, rb0, rbl, nrb, whole, slot);
+                else
+                    merge_waves<1>(p, ring, merge_m, merge_l, b, rb0, rbl, nrb, whole, slot);
             }
             __syncthreads();
         }

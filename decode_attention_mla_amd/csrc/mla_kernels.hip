@@ -378,58 +378,26 @@ __device__ inline void read_vt8(s16x4 (&va)[kOutTiles], const uint32_t (&v)[4]) 
         : "memory");
 }
 
-// Eight transposing V^T reads, tiles 2G and 2G+1 of blocks A and B (tile ct
-// at base[ct % 4] + 1024 (ct / 4)), issued without waiting.  The results
-// are only defined after vt_wait4 on the same registers: that statement
-// names them as read-write operands, so the compiler cannot read, copy or
-// reuse them while the loads are in flight.
-template <int G>
-__device__ inline void vt_issue4(s16x4 (&d)[4], const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
-    constexpr int c0 = (2 * G) & 3, c1 = (2 * G + 1) & 3, off = 1024 * ((2 * G) >> 2);
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%8\n"
-        "ds_read_b64_tr_b16 %1, %5 offset:%8\n"
-        "ds_read_b64_tr_b16 %2, %6 offset:%8\n"
-        "ds_read_b64_tr_b16 %3, %7 offset:%8"
-        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
-        : "v"(vA[c0]), "v"(vB[c0]), "v"(vA[c1]), "v"(vB[c1]), "n"(off)
-        : "memory");
-}
-
-// Tiles 4Q .. 4Q+3 of blocks A and B (eight reads), issued without waiting:
-// d[2j], d[2j+1] are tile 4Q+j of A and B.  Complete after vt_wait8.
+// Eight transposing V^T reads, tiles 4Q .. 4Q+3 of blocks A and B (tile ct
+// at base[ct % 4] + 1024 (ct / 4)): d[2j] and d[2j+1] are tile 4Q+j of A
+// and B.  Waited for inside the same statement, like read_vt8.
 template <int Q>
-__device__ inline void vt_issue_group(s16x4 (&d)[8], const uint32_t (&vA)[4], const uint32_t (&vB)[4]);
-
-__device__ inline void vt_wait8(s16x4 (&d)[8]) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]),
-                   "+v"(d[7])
-                 :
-                 : "memory");
-}
-
-__device__ inline void vt_wait4(s16x4 (&d)[4]) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]) :: "memory");
-}
-
-template <int Q>
-__device__ inline void vt_issue_group(s16x4 (&d)[8], const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
-    vt_issue4<2 * Q>(*reinterpret_cast<s16x4(*)[4]>(&d[0]), vA, vB);
-    vt_issue4<2 * Q + 1>(*reinterpret_cast<s16x4(*)[4]>(&d[4]), vA, vB);
-}
-
-// Four transposing V^T reads of one block, tiles 4G .. 4G+3, issued without
-// waiting (complete after vt_wait4).
-template <int G>
-__device__ inline void vt_issue_tiles4(s16x4 (&d)[4], const uint32_t (&v)[4]) {
+__device__ inline void read_pair_group(s16x4 (&d)[8], const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
+    constexpr int off0 = 1024 * ((4 * Q) >> 2);  // tiles 4Q .. 4Q+3 share one 1 KB slice
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%8\n"
-        "ds_read_b64_tr_b16 %1, %5 offset:%8\n"
-        "ds_read_b64_tr_b16 %2, %6 offset:%8\n"
-        "ds_read_b64_tr_b16 %3, %7 offset:%8"
-        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
-        : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "n"(1024 * G)
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]),
+          "=&v"(d[7])
+        : "v"(vA[0]), "v"(vB[0]), "v"(vA[1]), "v"(vB[1]), "v"(vA[2]), "v"(vB[2]), "v"(vA[3]), "v"(vB[3]),
+          "n"(off0)
         : "memory");
 }
 
@@ -473,8 +441,7 @@ __device__ inline void block_scores(float (&sv)[4], float &mx, s16x4 (&va)[kOutT
 // the lane's own P^T values (head l%16, keys 4g + i: the score accumulator
 // layout) as {hi[0..3], lo[0..3]}, and the A operand the lane's transposed
 // V^T read (channel l%16, keys 4g + i) twice: sum_k A B = V^T (P_hi + P_lo).
-// Tiles 0..7 were read with the scores; the others are read four at a time,
-// each group in flight while the MFMAs of the previous four run.
+// Tiles 0..7 were read with the scores; the others are read eight at a time.
 __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)[kOutTiles],
                                 const uint32_t (&v_addr)[4]) {
     s16x8 pb;
@@ -489,30 +456,23 @@ __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)
     }
     const bf16x8 p8 = __builtin_bit_cast(bf16x8, pb);
     st.l += psum;
-    // Group k = tiles 4k .. 4k+3: groups 0 and 1 are in va, group k >= 2 in
-    // buf[k & 1], issued while the MFMAs of group k-1 run.
-    s16x4 buf[2][4];
+    // Tiles 8G .. 8G+7: group 0 was read with the scores; group G+1 is read
+    // once the MFMAs of group G are issued, so its reads overlap them.
 #pragma unroll
-    for (int g = 0; g < kOutTiles / 4; ++g) {
-        switch (g + 1) {
-        case 2: vt_issue_tiles4<2>(buf[0], v_addr); break;
-        case 3: vt_issue_tiles4<3>(buf[1], v_addr); break;
-        case 4: vt_issue_tiles4<4>(buf[0], v_addr); break;
-        case 5: vt_issue_tiles4<5>(buf[1], v_addr); break;
-        case 6: vt_issue_tiles4<6>(buf[0], v_addr); break;
-        case 7: vt_issue_tiles4<7>(buf[1], v_addr); break;
-        default: break;
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < kOutTiles / 8; ++g) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ct = 4 * g + j;
-            const s16x4 a = g < 2 ? va[ct] : buf[g & 1][j];
-            const bf16x8 a8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3));
+        for (int j = 0; j < 8; ++j) {
+            const int ct = 8 * g + j;
+            const bf16x8 a8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va[ct], va[ct], 0, 1, 2, 3, 0, 1, 2, 3));
             st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, p8, st.acc[ct], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (g + 1 >= 2 && g + 1 < kOutTiles / 4) vt_wait4(buf[(g + 1) & 1]);
+        switch (g + 1) {  // compile-time after unrolling
+        case 1: read_vt8<1>(va, v_addr); break;
+        case 2: read_vt8<2>(va, v_addr); break;
+        case 3: read_vt8<3>(va, v_addr); break;
+        default: break;
+        }
     }
 }
 
@@ -574,27 +534,15 @@ __device__ inline void pair_pv(WaveState &st, const float (&sv)[8], const uint32
         plo[i] = static_cast<__bf16>(pr - static_cast<float>(h));
     }
     st.l += psum;
-    // Software pipeline over 8 groups of 4 tiles: the 8 reads of group q+1
-    // are in flight while the 8 MFMAs of group q run (long enough to cover
-    // an LDS round trip, which a pair of tiles was not).
+    // Groups of 4 tiles (8 reads each): group q+1 is read once the MFMAs of
+    // group q are issued, so its reads overlap them.  Two buffers: the reads
+    // never write registers an issued MFMA still reads.
     s16x4 buf[2][8];
-    vt_issue_group<0>(buf[0], vA, vB);
-    vt_wait8(buf[0]);
+    read_pair_group<0>(buf[0], vA, vB);
 #pragma unroll
     for (int q = 0; q < kOutTiles / 4; ++q) {
         s16x4 (&cur)[8] = buf[q & 1];
         s16x4 (&nxt)[8] = buf[(q + 1) & 1];
-        switch (q + 1) {  // compile-time after unrolling
-        case 1: vt_issue_group<1>(nxt, vA, vB); break;
-        case 2: vt_issue_group<2>(nxt, vA, vB); break;
-        case 3: vt_issue_group<3>(nxt, vA, vB); break;
-        case 4: vt_issue_group<4>(nxt, vA, vB); break;
-        case 5: vt_issue_group<5>(nxt, vA, vB); break;
-        case 6: vt_issue_group<6>(nxt, vA, vB); break;
-        case 7: vt_issue_group<7>(nxt, vA, vB); break;
-        default: break;
-        }
-        __builtin_amdgcn_sched_barrier(0);  // reads first, then this group's MFMAs
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int ct = 4 * q + j;
@@ -603,9 +551,17 @@ __device__ inline void pair_pv(WaveState &st, const float (&sv)[8], const uint32
             st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[ct], 0, 0, 0);
             st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[ct], 0, 0, 0);
         }
-        // Keep this group's MFMAs ahead of the wait for the next group's reads.
-        __builtin_amdgcn_sched_barrier(0);
-        if (q + 1 < kOutTiles / 4) vt_wait8(nxt);
+        __builtin_amdgcn_sched_barrier(0);  // this group's MFMAs issue before the next reads
+        switch (q + 1) {  // compile-time after unrolling
+        case 1: read_pair_group<1>(nxt, vA, vB); break;
+        case 2: read_pair_group<2>(nxt, vA, vB); break;
+        case 3: read_pair_group<3>(nxt, vA, vB); break;
+        case 4: read_pair_group<4>(nxt, vA, vB); break;
+        case 5: read_pair_group<5>(nxt, vA, vB); break;
+        case 6: read_pair_group<6>(nxt, vA, vB); break;
+        case 7: read_pair_group<7>(nxt, vA, vB); break;
+        default: break;
+        }
     }
 }
 

@@ -1,10 +1,10 @@
-"""The split kernel issues some LDS reads from inline assembly and waits for
-them in a later statement.  The compiler treats an asm output as written
-when the statement ends, so the kernel is only correct if no instruction
-reads, writes or copies those registers before the wait.  This test builds
-the gfx950 assembly with the library's own flags and checks exactly that
-(CPU only: hipcc cross-compiles)."""
-import os
+"""The split kernel issues some loads from inline assembly (transposing LDS
+reads, the query loads into accumulation registers).  The compiler takes an
+asm statement's outputs as written when the statement ends, so every such
+statement must wait for its own loads before it ends.  This test builds the
+gfx950 assembly with the library's own flags and checks exactly that, for
+every inline-asm block of the split kernel (CPU only: hipcc cross-compiles).
+"""
 import re
 import subprocess
 
@@ -14,13 +14,8 @@ from decode_attention_mla_amd import build as libbuild
 
 pytestmark = pytest.mark.slow
 
-
-def vregs(tok):
-    m = re.match(r"v\[(\d+):(\d+)\]", tok)
-    if m:
-        return set(range(int(m.group(1)), int(m.group(2)) + 1))
-    m = re.match(r"v(\d+)$", tok)
-    return {int(m.group(1))} if m else set()
+LDS_LOAD = re.compile(r"^ds_read")
+VMEM_LOAD = re.compile(r"^(global_load|buffer_load|flat_load)")
 
 
 @pytest.fixture(scope="module")
@@ -32,32 +27,49 @@ def asm(tmp_path_factory):
     return out.read_text().split("\n")
 
 
-def test_in_flight_transposed_reads_are_never_touched(asm):
-    issued = 0
-    pending = set()
-    for line in asm:
+def split_kernel(asm):
+    start = next(i for i, l in enumerate(asm) if l.startswith("_ZN3mla16mla_split_kernelENS_6ParamsE:"))
+    end = next(i for i in range(start, len(asm)) if asm[i].strip().startswith("s_endpgm"))
+    return asm[start:end + 1]
+
+
+def asm_blocks(lines):
+    """Instructions of each inline-asm statement, in order."""
+    blocks, cur = [], None
+    for line in lines:
         t = line.strip()
-        if t.startswith(".LBB") or t.startswith("s_endpgm") or t.startswith("s_branch") \
-                or t.startswith("s_cbranch"):
-            assert not pending, f"transposed read still in flight at block boundary: {t}"
-        if t.startswith("ds_read_b64_tr_b16"):
-            pending |= vregs(t.split()[1].rstrip(","))
-            issued += 1
+        if t.startswith(";;#ASMSTART"):
+            cur = []
+        elif t.startswith(";;#ASMEND"):
+            blocks.append(cur)
+            cur = None
+        elif cur is not None and t and not t.startswith(";"):
+            cur.append(t)
+    return blocks
+
+
+def test_inline_asm_loads_wait_in_their_own_statement(asm):
+    blocks = asm_blocks(split_kernel(asm))
+    checked = 0
+    for ins in blocks:
+        lds = [i for i in ins if LDS_LOAD.match(i)]
+        vmem = [i for i in ins if VMEM_LOAD.match(i)]
+        if not lds and not vmem:
             continue
-        if t.startswith("s_waitcnt") and "lgkmcnt(0)" in t:
-            pending = set()
-            continue
-        if not t or t.startswith(";") or t.startswith("."):
-            continue
-        ops = re.findall(r"v\[\d+:\d+\]|v\d+\b", t)
-        touched = set().union(*[vregs(o) for o in ops]) if ops else set()
-        assert not (touched & pending), f"in-flight register touched: {t}"
-    assert issued > 0, "no transposed reads found: the check is vacuous"
+        checked += 1
+        last = ins[-1]
+        assert last.startswith("s_waitcnt"), f"asm loads without a closing wait: {ins}"
+        if lds:
+            assert "lgkmcnt(0)" in last, f"LDS loads not waited for in their statement: {ins}"
+        if vmem:
+            assert "vmcnt(0)" in last, f"global loads not waited for in their statement: {ins}"
+        # nothing but the loads themselves before the closing wait
+        for i in ins[:-1]:
+            assert LDS_LOAD.match(i) or VMEM_LOAD.match(i), f"other work between asm loads and wait: {i}"
+    assert checked > 0, "no inline-asm loads found: the check is vacuous"
 
 
 def test_no_scratch_in_the_split_kernel(asm):
-    text = "\n".join(asm)
-    body = text[text.index("_ZN3mla16mla_split_kernelENS_6ParamsE:"):]
-    body = body[: body.index("s_endpgm")]
+    body = "\n".join(split_kernel(asm))
     assert "scratch_" not in body, "the split kernel spills to scratch"
     assert "v_pk_mul_f32" not in body and "v_pk_add_f32" not in body and "v_pk_fma_f32" not in body

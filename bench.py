@@ -84,6 +84,81 @@ def calibrate_copy(steps: int) -> None:
                       "ms_per_copy": dt * 1e3, "GBps_read_plus_write": 2 * n / dt / 1e9}))
 
 
+def sweep(args) -> int:
+    """The pages' sweep grid on one GPU: KV GB/s against context length at
+    batch 16 and 32 (16 heads), and against the per-GPU head count (16, 32,
+    64, 128) at batch 16 x 64K.  One JSON line per point.  Inputs are seeded
+    N(0,1) bf16 drawn on the device (a timing curve: parity is the tests'
+    job); workloads under 1 GiB rotate over copies so every step streams
+    from HBM."""
+    import numpy as np
+    import torch
+
+    import decode_attention_mla_amd as mla
+
+    gen = torch.Generator(device="cuda")
+    points = [(b, 1, 16, L) for b in (16, 32) for L in (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536)]
+    points += [(16, 1, h, 65536) for h in (32, 64, 128)]
+    if args.sweep_points:
+        keep = {tuple(int(x) for x in p.split("x")) for p in args.sweep_points.split(",")}
+        points = [pt for pt in points if (pt[0], pt[2], pt[3]) in keep] or \
+                 [(b, 1, h, L) for b, h, L in sorted(keep)]
+    ctx = mla.Context()
+    ctx.set_option(mla.MLA_OPT_NUM_SPLITS, args.splits)
+    ctx.set_option(mla.MLA_OPT_MIN_CHUNK, args.min_chunk)
+    scale = 1.0 / 24.0
+    for B, s_q, H, L in points:
+        gen.manual_seed(7000 + B * 131 + H * 17 + L)
+        q = torch.randn((B, s_q, H, 576), generator=gen, device="cuda").to(torch.bfloat16)
+        kv = torch.randn((B, L, 576), generator=gen, device="cuda").to(torch.bfloat16)
+        lens_h = np.full(B, L, dtype=np.int32)
+        lens = torch.from_numpy(lens_h).cuda()
+        kv_bytes = B * L * 576 * 2
+        copies = [kv]
+        while kv_bytes * len(copies) < (1 << 30) and len(copies) < 16:
+            copies.append(kv.clone())
+        out = torch.empty((B, s_q, H, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device="cuda")
+        ctx.reserve(s_q, H)
+
+        def step(i):
+            mla.mla_decode(ctx, q, copies[i % len(copies)], None, lens, scale, out=out, lse=lse,
+                           seqlens_host=lens_h)
+
+        s0 = time.perf_counter()
+        while time.perf_counter() - s0 < args.settle_s:
+            for i in range(10):
+                step(i)
+            torch.cuda.synchronize()
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / args.steps
+        ctx.kernel_times()
+        ctx.set_option(mla.MLA_OPT_KERNEL_TIMING, 1)
+        for i in range(args.steps):
+            step(i)
+        split_ms, n_split, comb_ms, n_comb = ctx.kernel_times()
+        ctx.set_option(mla.MLA_OPT_KERNEL_TIMING, 0)
+        split_us = split_ms * 1e3 / max(1, n_split)
+        print(json.dumps({"mode": "sweep", "batch": B, "s_q": s_q, "heads": H, "kv_len": L,
+                          "min_chunk": args.min_chunk or "default",
+                          "kv_bytes": kv_bytes, "us_per_call": round(us, 2),
+                          "GBps": round(kv_bytes / us / 1e3, 1),
+                          "split_us": round(split_us, 2),
+                          "split_GBps": round(kv_bytes / split_us / 1e3, 1),
+                          "split_frac_of_8TBps": round(kv_bytes / split_us / 1e3 / PEAK_HBM_GBS, 4),
+                          "combine_us": round(comb_ms * 1e3 / n_comb, 2) if n_comb else 0.0}), flush=True)
+        del q, kv, copies, out, lse
+        torch.cuda.empty_cache()
+    ctx.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +171,10 @@ def main() -> int:
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="untimed steps for this long before the warmup steps (clock ramp)")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="GB/s against context length (bs16, bs32) and head count; one line per point")
+    ap.add_argument("--sweep-points", default="",
+                    help="restrict the sweep to BxHxL points, comma-separated (e.g. 16x16x512)")
     ap.add_argument("--splits", type=int, default=0, help="key ranges per launch (0: library default)")
     ap.add_argument("--min-chunk", type=int, default=0, help="smallest key range (0: library default)")
     args = ap.parse_args()
@@ -115,6 +194,8 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy(max(1, args.steps))
         return 0
+    if args.sweep:
+        return sweep(args)
 
     name = args.workload or wl.HEADLINE
     w = wl.WORKLOADS[name]

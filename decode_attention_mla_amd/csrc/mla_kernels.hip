@@ -790,7 +790,8 @@ void mla_split_kernel(Params p) {
             } else {
                 // Several row blocks: the producer wave of each key group
                 // loads its steps into a shared ring of two; a barrier per
-                // step publishes it and frees the slots read one step ago.
+                // step publishes it and frees the slots read one step ago,
+                // which then take the step after it.
                 const int n_kg = n_mine, pstep = kstep;
                 const int key_end = min(vis_end, seg_hi);
                 char *slots = first;
@@ -810,15 +811,10 @@ void mla_split_kernel(Params p) {
                     uint32_t vA[4] = {0, 0, 0, 0}, vB[4] = {0, 0, 0, 0};
                     bool lagged = false;
                     for (; i < n_iter; ++i) {
-                        if (producer) {
-                            if (i + 1 < n_kg) {
-                                issue_pair(i + 1);
-                                wait_vm<2 * kQkSteps>();  // step i landed, step i+1 may fly
-                            } else {
-                                wait_vm<0>();
-                            }
-                        }
+                        if (producer) wait_vm<0>();  // step i landed (its only loads in flight)
                         bare_barrier();  // step i is in; every wave is done with step i-1
+                        // Only now is step i-1's slot free for step i+1.
+                        if (producer && i + 1 < n_kg) issue_pair(i + 1);
                         const int kb = kfirst + i * pstep;
                         if (active && i < n_kg && kb < vis_end) {
                             const char *stA = slots + (i & 1) * 2 * kBlockBytes;

@@ -23,6 +23,9 @@ FLAGS = [
     "-shared",
     # no packed fp32 arithmetic in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in vector registers: the kernels scale them with
+    # vector ALU (softmax rescale), which cannot read accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-I", os.path.join(PKG, "csrc"),
 ]

@@ -14,27 +14,29 @@
 // Work decomposition (one workgroup = 4 waves of 64 lanes):
 //   * A "row block" is 16 query rows: the 16 heads h0..h0+15 of one token.
 //   * Workgroup (g, y) owns key range g of the split plan (plan.h) and row
-//     blocks 4y .. 4y+3.  With fewer than 4 row blocks the spare waves split
-//     the keys: wave w takes row block w % nrb and every nkg-th 16-key block.
-//   * Each wave is an independent flash-decoding worker: its own running
-//     max / sum / O accumulator, no barrier inside the key loop.  The waves
-//     of a segment are merged through LDS at the end, and the result is
-//     either the final output or a partial for the combine kernel.
+//     blocks 4y .. 4y+3 (nrb of them).  How they share the keys is the
+//     kernel's mode (SplitMode): with one row block the four waves split the
+//     keys, each an independent flash-decoding worker over every 4th 16-key
+//     block with a private LDS ring and no barrier; with two to four the
+//     waves of a key group compute the same 32-key steps for different row
+//     blocks, fed through a shared two-slot LDS ring, one barrier per step.
+//   * At the end of a segment (the range's part of one sequence) the waves'
+//     results are merged (through LDS where several waves share a row
+//     block) into the final rows or into a partial for the combine kernel.
 //
-// Per 16-key block, per wave:
-//   1. 18 x 16-byte loads per lane bring the 16 latent rows (1152 B each)
-//      straight into MFMA A-operand layout: lane l holds key l%16, channels
-//      32s + 8(l/16) .. +7.  The next block's loads are in flight while the
-//      current one is computed (register double buffer).
-//   2. S^T (16 keys x 16 heads) = 18 MFMA 16x16x32 bf16, fp32 accumulate.
-//   3. The 512 value channels are written to a wave-private LDS tile
-//      (XOR-swizzled 16-byte chunks) for the transposed read PV needs.
-//   4. Online softmax in fp32 (log2 domain); row max over keys = in-lane max
-//      of 4 + two cross-lane xor shuffles; the O rescale is skipped when no
-//      head's max moved.
-//   5. O^T (512 ch x 16 heads) += V^T P^T with 32 + 32 MFMA 16x16x16 bf16:
-//      P is split into bf16 hi + lo parts so that rounding P costs no
-//      accuracy (bf16 P alone gives O errors near 1e-4 at short contexts).
+// Per 16 keys, per wave:
+//   1. The 16 latent rows (1152 B each) arrive by direct-to-LDS 16-byte
+//      loads, whole 128-byte lines, XOR-swizzled so that both operand reads
+//      below are bank-conflict free; the next block or step is in flight
+//      while the current one is computed.
+//   2. S^T (16 keys x 16 heads) = 18 MFMA 16x16x32 bf16, fp32 accumulate;
+//      the K operand is read from LDS, Q^T stays in registers.
+//   3. Online softmax in fp32 (log2 domain); the accumulators are rescaled
+//      only when a block's max passes the reference max by kMaxLag.
+//   4. O^T (512 ch x 16 heads) += V^T P^T: 32 MFMA 16x16x32 bf16 per 16
+//      keys, P split into bf16 hi + lo halves (so that rounding P costs no
+//      accuracy) that the MFMA's k index carries; V^T comes from
+//      transposing LDS reads.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -47,6 +49,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "mla_decode.h"
@@ -65,9 +68,10 @@ constexpr int kBlockBytes = kKeyBlock * kDqk * 2;         // 18 KB: one 16-key b
 constexpr int kStages = 2;                                 // LDS ring depth per wave
 constexpr int kStageBytes = kWaves * kBlockBytes;          // one stage of all waves: 72 KB
 // Shared rings (several row blocks per workgroup): per key group two 32-key
-// steps of two blocks each, one computed while the next is in flight.
-constexpr int kPairSlots = 4;
-static_assert(2 * kPairSlots * kBlockBytes <= kStages * kStageBytes, "ring size");
+// steps of two blocks each, one computed while the next is in flight; the
+// slot of parity s of key group kg is blocks 2kg, 2kg + 1 of stage array s.
+constexpr int kPairBytes = 2 * kBlockBytes;
+static_assert(2 * kPairBytes <= kStageBytes, "two key groups' slots fit in a stage array");
 constexpr int kMergePitch = kDv + 4;           // floats per merge row (bank spread)
 constexpr int kMergeWaveFloats = 16 * kMergePitch;          // one wave's O: 33 KB
 static_assert(2 * kMergeWaveFloats * 4 + kWaves * 16 * 2 * 4 <= kStageBytes,
@@ -103,6 +107,7 @@ struct Params {
     int32_t max_pages;
     int32_t n_rb;      // row blocks: s_q * heads / 16
     int32_t splits;    // key ranges (gridDim.x of the split kernel when sized blind)
+    int32_t y0;        // row-block group of blockIdx.y == 0
     float scale_log2;  // scale * log2(e)
 };
 
@@ -288,6 +293,83 @@ __device__ inline void issue_block(char *stage, const BlockCtx &c, int kb, int64
             (__attribute__((address_space(3))) void *)(stage + t * 1024), 16, 0, kNonTemporal);
 }
 
+// The same 18 loads in buffer form, for the shared kernel: a buffer
+// resource spans the block's real rows, so rows past the last key read as
+// zeros (they are masked out, and zero rows keep P V finite).  The compiler
+// counts buffer-form direct loads on the vector-memory counter only, so the
+// LDS reads issued while they fly keep exact waits; in the FLAT form it
+// makes every such wait a full one.  vrow[h] is the lane's byte offset of
+// its 16 bytes in rows 8h .. 8h+7 (row 8h + l/8, chunk (l%8) ^ swz(l/8)).
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit data format
+constexpr int kQuarter = 2 * kQkSteps / kWaves;  // loads per wave per step with one key group
+static_assert(kQkSteps * 1024 == kBlockBytes, "block B's slices follow block A's");
+template <int T>
+__device__ inline void buffer_load_slice(__amdgpu_buffer_rsrc_t rs, char *stage, const int (&vrow)[2]) {
+    // The column-group offset goes in the scalar offset: an instruction
+    // offset would move the LDS destination as well.
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(stage + T * 1024), 16,
+                                             vrow[T / 9], 128 * (T % 9), 0, kNonTemporal);
+}
+template <int... T>
+__device__ inline void buffer_load_slices(__amdgpu_buffer_rsrc_t rs, char *stage, const int (&vrow)[2],
+                                          std::integer_sequence<int, T...>) {
+    (buffer_load_slice<T>(rs, stage, vrow), ...);
+}
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const BlockCtx &c, int kb, int64_t page);
+__device__ inline void issue_block_buffer(char *stage, const BlockCtx &c, int kb, int64_t page,
+                                          const int (&vrow)[2]) {
+    buffer_load_slices(block_rsrc(c, kb, page), stage, vrow, std::make_integer_sequence<int, kQkSteps>{});
+}
+
+// One wave's share of the 36 loads of a 32-key step (blocks A at kb and B
+// at kb + 16, in buffer form): slices share, share + nshare, ... of the
+// step's 36 (block A's 18, then block B's), so that the waves that compute
+// a step also split its loads.  block_rsrc: the descriptor of the block at
+// kb.  A block wholly past the last key (the second block of a sequence's
+// last step) gets an empty range: nothing is read and the stage fills with
+// zeros.  The descriptor must be wave-uniform (scalar registers);
+// readfirstlane states it, else the compiler wraps every load in a
+// per-lane loop.
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const BlockCtx &c, int kb, int64_t page) {
+    const uint16_t *row0 = c.page_size ? c.kv + (page * c.page_size + kb % c.page_size) * (int64_t)kDqk
+                                       : c.kv + (c.seq_base + kb) * (int64_t)kDqk;
+    const int rows = max(0, min(kKeyBlock, c.last_key + 1 - kb));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)uniform((int64_t)(uintptr_t)row0), 0,
+                                             uniform(rows * kDqk * 2), kBufferWord3);
+}
+__device__ inline void issue_step_share(char *dst, const BlockCtx &c, int kb, int64_t page_a, int64_t page_b,
+                                        const int (&vrow)[2], int share, int nshare) {
+    const __amdgpu_buffer_rsrc_t ra = block_rsrc(c, kb, page_a);
+    const __amdgpu_buffer_rsrc_t rb = block_rsrc(c, kb + kKeyBlock, page_b);
+    for (int idx = share; idx < 2 * kQkSteps; idx += nshare) {
+        const bool hb = idx >= kQkSteps;
+        const int t = hb ? idx - kQkSteps : idx;
+        // Slice t of block A or B sits at 1024 idx in the step's image.
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb ? rb : ra,
+                                                 (__attribute__((address_space(3))) void *)(dst + 1024 * idx), 16,
+                                                 t < 9 ? vrow[0] : vrow[1], 128 * (t < 9 ? t : t - 9), 0,
+                                                 kNonTemporal);
+    }
+}
+
+// This wave's quarter of a step's loads (kOneGroup): slices share + 4k,
+// k < 9, of the step's 36 (block A's 18, then block B's), unrolled.
+__device__ inline void issue_step_quarter(char *dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          const int (&vrow)[2], int share) {
+#pragma unroll
+    for (int k = 0; k < kQuarter; ++k) {
+        const int idx = share + kWaves * k;
+        const bool hb = idx >= kQkSteps;
+        const int t = hb ? idx - kQkSteps : idx;
+        // Slice t of block A or B sits at 1024 idx in the step's image (a
+        // plain offset, so the compiler still sees which array is written).
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb ? rb : ra,
+                                                 (__attribute__((address_space(3))) void *)(dst + 1024 * idx), 16,
+                                                 t < 9 ? vrow[0] : vrow[1], 128 * (t < 9 ? t : t - 9), 0,
+                                                 kNonTemporal);
+    }
+}
+
 // Per-lane byte offsets of the operand reads within a block image.
 //  K operand of QK^T step t (lane l -> key k = l%16, chunk 4t + l/16):
 //    slice 9(k/8) + t/2, slot 8(k%8) + ((4(t%2) + l/16) ^ swz(k%8)),
@@ -378,29 +460,6 @@ __device__ inline void read_vt8(s16x4 (&va)[kOutTiles], const uint32_t (&v)[4]) 
         : "memory");
 }
 
-// Eight transposing V^T reads, tiles 4Q .. 4Q+3 of blocks A and B (tile ct
-// at base[ct % 4] + 1024 (ct / 4)): d[2j] and d[2j+1] are tile 4Q+j of A
-// and B.  Waited for inside the same statement, like read_vt8.
-template <int Q>
-__device__ inline void read_pair_group(s16x4 (&d)[8], const uint32_t (&vA)[4], const uint32_t (&vB)[4]) {
-    constexpr int off0 = 1024 * ((4 * Q) >> 2);  // tiles 4Q .. 4Q+3 share one 1 KB slice
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%16\n"
-        "ds_read_b64_tr_b16 %1, %9 offset:%16\n"
-        "ds_read_b64_tr_b16 %2, %10 offset:%16\n"
-        "ds_read_b64_tr_b16 %3, %11 offset:%16\n"
-        "ds_read_b64_tr_b16 %4, %12 offset:%16\n"
-        "ds_read_b64_tr_b16 %5, %13 offset:%16\n"
-        "ds_read_b64_tr_b16 %6, %14 offset:%16\n"
-        "ds_read_b64_tr_b16 %7, %15 offset:%16\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]),
-          "=&v"(d[7])
-        : "v"(vA[0]), "v"(vB[0]), "v"(vA[1]), "v"(vB[1]), "v"(vA[2]), "v"(vB[2]), "v"(vA[3]), "v"(vB[3]),
-          "n"(off0)
-        : "memory");
-}
-
 // Scores of one block: S^T[key][head] for 16 keys x 16 heads, scaled into
 // the log2 domain and masked; lane l holds head l%16, keys kb + 4(l/16) + i
 // and mx is the block max of its head.  The A operand K comes from the
@@ -476,95 +535,6 @@ __device__ inline void block_pv(WaveState &st, const float (&sv)[4], s16x4 (&va)
     }
 }
 
-// ---- 32-key steps (shared rings): two 16-key blocks A and B per step ----
-//
-// Scores of both blocks (sv[0..3] from A, sv[4..7] from B, lane l: head
-// l%16, keys 4(l/16) + i of each block) and their joint max.
-__device__ inline void pair_scores(float (&sv)[8], float &mx, const char *stA, const char *stB,
-                                   const int (&k_off)[2], const bf16x8 (&qf)[kQkSteps], int kbA,
-                                   int kbB, int key_end, float scale_log2, int lane) {
-    bf16x8 ka[2][kQkSteps];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < kQkSteps; ++t)
-            ka[h][t] = *reinterpret_cast<const bf16x8 *>((h ? stB : stA) + k_off[t & 1] +
-                                                         1024 * (t >> 1));
-    // All 36 K reads are issued before the first MFMA waits on one of them.
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 s[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < kQkSteps; t += 2) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][t], qf[t], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][t + 1], qf[t + 1], s1, 0, 0, 0);
-        }
-        s[h] = s0 + s1;
-    }
-    const int kA = kbA + 4 * (lane >> 4), kB = kbB + 4 * (lane >> 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sv[i] = (kA + i < key_end) ? s[0][i] * scale_log2 : -INFINITY;
-        sv[4 + i] = (kB + i < key_end) ? s[1][i] * scale_log2 : -INFINITY;
-    }
-    mx = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-}
-
-// O^T += V^T P^T over 32 keys with 16x16x32 MFMAs.  Both operands use the
-// same k order: slot 8(l/16) + i is key 4(l/16) + i of block A for i < 4 and
-// key 4(l/16) + i - 4 of block B for i >= 4.  P^T (B operand) is the
-// joined score registers; V^T (A operand) joins one transposing read of
-// each block.
-__device__ inline void pair_pv(WaveState &st, const float (&sv)[8], const uint32_t (&vA)[4],
-                               const uint32_t (&vB)[4]) {
-    bf16x8 phi, plo;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(sv[i] - st.m);
-        psum += pr;
-        const __bf16 h = static_cast<__bf16>(pr);
-        phi[i] = h;
-        plo[i] = static_cast<__bf16>(pr - static_cast<float>(h));
-    }
-    st.l += psum;
-    // Groups of 4 tiles (8 reads each): group q+1 is read once the MFMAs of
-    // group q are issued, so its reads overlap them.  Two buffers: the reads
-    // never write registers an issued MFMA still reads.
-    s16x4 buf[2][8];
-    read_pair_group<0>(buf[0], vA, vB);
-#pragma unroll
-    for (int q = 0; q < kOutTiles / 4; ++q) {
-        s16x4 (&cur)[8] = buf[q & 1];
-        s16x4 (&nxt)[8] = buf[(q + 1) & 1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ct = 4 * q + j;
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(cur[2 * j], cur[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[ct], 0, 0, 0);
-            st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[ct], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // this group's MFMAs issue before the next reads
-        switch (q + 1) {  // compile-time after unrolling
-        case 1: read_pair_group<1>(nxt, vA, vB); break;
-        case 2: read_pair_group<2>(nxt, vA, vB); break;
-        case 3: read_pair_group<3>(nxt, vA, vB); break;
-        case 4: read_pair_group<4>(nxt, vA, vB); break;
-        case 5: read_pair_group<5>(nxt, vA, vB); break;
-        case 6: read_pair_group<6>(nxt, vA, vB); break;
-        case 7: read_pair_group<7>(nxt, vA, vB); break;
-        default: break;
-        }
-    }
-}
-
 // Move the reference max up to the block max and rescale (rare path).
 __device__ inline void rescale(WaveState &ws, float mx) {
     const float m_new = fmaxf(ws.m, mx);
@@ -581,21 +551,148 @@ __device__ inline void rescale(WaveState &ws, float mx) {
 // the same softmax; the rescale sits outside the hot loop.
 constexpr float kMaxLag = 8.0f;
 
+// ---- 32-key steps (shared rings): two 16-key blocks A and B per step ----
+
+// One transposing V^T read, issued through the compiler's builtin so that it
+// tracks the result and waits for it only where it is used.  Within 16
+// lanes, lane i receives element i % 4 of the rows addressed by lanes
+// i / 4 + 4r.
+__device__ inline s16x4 read_vt(const char *addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(addr));
+}
+
+// Max of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that
+// hold one head's keys), with row-swapping permutes instead of LDS
+// permutes: those would join the LDS counter, and waiting for their result
+// would wait for every operand read issued before them.  Each swap of x
+// with itself returns, per lane, x of the lane and of its partner.
+__device__ inline float max_over_lane_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Compile-time slot parity of a shared-ring step.
+template <int V>
+struct Parity {
+    static constexpr int value = V;
+};
+
+// The operand reads of one 32-key step of a row block form one stream: the
+// 36 K reads (block A's 18 k-steps, then block B's) and then the 64 V^T
+// reads (tile ct of block A is read 2ct, of block B 2ct + 1).  Each MFMA of
+// the step is issued together with the read kAhead places further down the
+// stream, so LDS latency overlaps the MFMAs instead of adding to them; the
+// order is pinned with scheduling barriers and the compiler places the
+// waits.
+constexpr int kPairK = 2 * kQkSteps;
+constexpr int kPairV = 2 * kOutTiles;
+constexpr int kAhead = 12;
+static_assert(kAhead <= kPairK, "the stream starts with K reads");
+
+
+struct PairReads {
+    const char *stA, *stB;  // the step's blocks A and B
+    int k_off[2];
+    uint32_t v_off[4];
+    bf16x8 ka[kPairK];
+    s16x4 vr[kPairV];
+
+    __device__ void read(int r) {
+        if (r < kPairK) {
+            const int t = r % kQkSteps;
+            ka[r] = *reinterpret_cast<const bf16x8 *>((r < kQkSteps ? stA : stB) + k_off[t & 1] +
+                                                      1024 * (t >> 1));
+        } else if (r < kPairK + kPairV) {
+            const int v = r - kPairK, ct = v >> 1;
+            vr[v] = read_vt(((v & 1) ? stB : stA) + v_off[ct & 3] + 1024 * (ct >> 2));
+        }
+    }
+};
+
+// Scores of a step: lane l holds head l%16, keys 4(l/16) + i of block A
+// (sv[i]) and of block B (sv[4 + i]), scaled into the log2 domain and
+// masked; mx is their max over the head.  Leaves the first kAhead V^T reads
+// of the stream in flight.
+__device__ inline void pair_scores(PairReads &rd, float (&sv)[8], float &mx, const bf16x8 (&qf)[kQkSteps],
+                                   int kbA, int key_end, float scale_log2, int lane) {
+#pragma unroll
+    for (int r = 0; r < kAhead; ++r) rd.read(r);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+#pragma unroll
+    for (int n = 0; n < kPairK; ++n) {
+        const int h = n / kQkSteps, t = n % kQkSteps;
+        s[h][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rd.ka[n], qf[t], s[h][t & 1], 0, 0, 0);
+        rd.read(n + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int kA = kbA + 4 * (lane >> 4), kB = kA + kKeyBlock;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sv[i] = (kA + i < key_end) ? (s[0][0][i] + s[0][1][i]) * scale_log2 : -INFINITY;
+        sv[4 + i] = (kB + i < key_end) ? (s[1][0][i] + s[1][1][i]) * scale_log2 : -INFINITY;
+    }
+    mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    mx = max_over_lane_groups(mx);
+}
+
+// P = exp2(s - m) and O^T += V^T P^T over the step's 32 keys, continuing
+// the stream at V^T read kAhead.  k slot 8(l/16) + i of a 16x16x32 MFMA is
+// key 4(l/16) + i of block A for i < 4 and of block B for i >= 4, in both
+// operands: P^T (B operand) is the joined score registers, split into bf16
+// hi and lo halves (two MFMAs per tile), and V^T (A operand) joins one
+// transposing read of each block.  Within a group of four tiles the hi
+// MFMAs come before the lo ones, so no MFMA waits on the one before it.
+__device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8]) {
+    bf16x8 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(sv[i] - ws.m);
+        psum += pr;
+        const __bf16 hb = static_cast<__bf16>(pr);
+        phi[i] = hb;
+        plo[i] = static_cast<__bf16>(pr - static_cast<float>(hb));
+    }
+    ws.l += psum;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 2 * kOutTiles; ++m) {
+        const int ct = 4 * (m >> 3) + (m & 3);
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(rd.vr[2 * ct], rd.vr[2 * ct + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        ws.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (m & 4) ? plo : phi, ws.acc[ct], 0, 0, 0);
+        rd.read(kPairK + kAhead + m);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // ------------------------------------------------- merging a segment's waves
 
-// After a segment the ring holds the waves' O rows for the merge: waves 0
-// and 1 in the first stage, waves 2 and 3 (and the stats) in the second.
-__device__ inline float *merge_row_at(char *ring, int w, int head) {
-    return reinterpret_cast<float *>(ring + (w < 2 ? 0 : kStageBytes)) + ((w & 1) * 16 + head) * kMergePitch;
-}
+// Where the waves' O rows and softmax stats go for the merge at the end of
+// a segment (the two stage arrays, reused): waves 0 and 1 in the first,
+// waves 2 and 3 and the stats (m, l: kWaves x 16 each) in the second.  (The
+// address is computed, not looked up: an array of pointers indexed by the
+// wave would be placed in memory.)
+struct MergeArea {
+    char *stage0, *stage1;
+    float *m, *l;
+    __device__ float *row(int w, int head) const {
+        return reinterpret_cast<float *>(w < 2 ? stage0 : stage1) + ((w & 1) * 16 + head) * kMergePitch;
+    }
+};
 
 // Rows of row block rb0 + rbl from the NKG waves that computed them (waves
 // rbl + nrb kg): the LSE-weighted sum of their O rows, normalized, written
 // as the final rows (whole) or as the segment's part.  Every LDS read is
 // issued before the first is used.  256 threads: 16 heads x 16 quads.
 template <int NKG>
-__device__ inline void merge_waves(const Params &p, char *ring, const float *merge_m, const float *merge_l,
-                                   int b, int rb0, int rbl, int nrb, bool whole, int slot) {
+__device__ inline void merge_waves(const Params &p, const MergeArea &ma, int b, int rb0, int rbl, int nrb,
+                                   bool whole, int slot) {
     const int head = threadIdx.x >> 4;
     const int cq = threadIdx.x & 15;
     float mw[NKG], lw[NKG];
@@ -603,11 +700,11 @@ __device__ inline void merge_waves(const Params &p, char *ring, const float *mer
 #pragma unroll
     for (int kg = 0; kg < NKG; ++kg) {
         const int w = rbl + nrb * kg;
-        mw[kg] = merge_m[w * 16 + head];
-        lw[kg] = merge_l[w * 16 + head];
+        mw[kg] = ma.m[w * 16 + head];
+        lw[kg] = ma.l[w * 16 + head];
 #pragma unroll
         for (int jc = 0; jc < kDv / 64; ++jc)
-            ov[jc][kg] = *reinterpret_cast<const f32x4 *>(merge_row_at(ring, w, head) + 4 * cq + 64 * jc);
+            ov[jc][kg] = *reinterpret_cast<const f32x4 *>(ma.row(w, head) + 4 * cq + 64 * jc);
     }
     __builtin_amdgcn_sched_barrier(0);
     float M = mw[0];
@@ -643,17 +740,86 @@ __device__ inline void merge_waves(const Params &p, char *ring, const float *mer
     }
 }
 
+// A wave that alone computed its row block (one key group) writes the rows
+// straight from its accumulators: normalized O (lane l: head l%16, channels
+// 16ct + 4(l/16) .. +3 of tile ct) and the LSE, as the final rows (whole)
+// or as the segment's part (log2-domain LSE).  Same values as merge_waves<1>.
+__device__ inline void write_rows(const Params &p, const WaveState &ws, int b, int rb, bool whole, int slot,
+                                  int lane) {
+    const int head = lane & 15, grp = lane >> 4;
+    float lt = ws.l;
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse2 = lt > 0.f ? ws.m + log2f(lt) : -INFINITY;
+    const int hpt = p.heads >> 4;
+    const int64_t row = ((int64_t)b * p.s_q + rb / hpt) * p.heads + (rb % hpt) * 16 + head;
+    float *orow;
+    if (whole) {
+        orow = p.out + row * kDv;
+        if (grp == 0) p.lse[row] = lse2 * kLn2;
+    } else {
+        const int64_t r = ((int64_t)slot * p.n_rb + rb) * 16 + head;
+        orow = p.part_o + r * kDv;
+        if (grp == 0) p.part_lse[r] = lse2;
+    }
+#pragma unroll
+    for (int ct = 0; ct < kOutTiles; ++ct)
+        *reinterpret_cast<f32x4 *>(orow + 16 * ct + 4 * grp) = ws.acc[ct] * inv;
+}
+
 // --------------------------------------------------------------- split kernel
 
+// How a workgroup's row blocks (nrb of them, of 16 query rows each) share
+// the keys:
+//  kOneBlock   nrb = 1: each wave streams its own 16-key blocks through a
+//              private two-stage ring, no barrier.
+//  kTwoGroups  nrb = 2: two key groups of two waves; the waves of a group
+//              share each 32-key step through a two-slot ring.
+//  kOneGroup   nrb = 3, 4: one key group of four waves sharing each 32-key
+//              step through a two-slot ring; all four waves issue a quarter
+//              of each step's loads, and each wave writes its rows itself.
+enum SplitMode { kOneBlock = 0, kTwoGroups = 1, kOneGroup = 2 };
+constexpr int kOneGroupSlot = kPairBytes;  // 36 KB: one step
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_split_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) char ring[kStages * kStageBytes];
+    constexpr bool kShared = kMode != kOneBlock;
+    char *stage0_base, *stage1_base;  // kOneBlock, kTwoGroups
+    MergeArea ma{};
+    if constexpr (kMode == kOneGroup) {
+        // Two step-sized arrays, the ring's slots.  The compiler tells LDS
+        // accesses of distinct arrays apart, so its own reads of one slot
+        // never wait for direct loads still landing in the other.  (Each
+        // wave writes its rows itself: no merge area.)
+        __shared__ __attribute__((aligned(16))) char slot_a[kOneGroupSlot];
+        __shared__ __attribute__((aligned(16))) char slot_b[kOneGroupSlot];
+        stage0_base = slot_a;
+        stage1_base = slot_b;
+    } else {
+        if constexpr (kMode == kTwoGroups) {
+            // Two stage arrays, for the same reason.
+            __shared__ __attribute__((aligned(16))) char stage_a[kStageBytes];
+            __shared__ __attribute__((aligned(16))) char stage_b[kStageBytes];
+            stage0_base = stage_a;
+            stage1_base = stage_b;
+        } else {
+            __shared__ __attribute__((aligned(16))) char ring[kStages * kStageBytes];
+            stage0_base = ring;
+            stage1_base = ring + kStageBytes;
+        }
+        ma.stage0 = stage0_base;
+        ma.stage1 = stage1_base;
+        ma.m = reinterpret_cast<float *>(stage1_base) + 2 * kMergeWaveFloats;
+        ma.l = ma.m + kWaves * 16;
+    }
     const int lane = threadIdx.x & 63;
     // Wave-uniform (scalar) so that stage addresses stay in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = blockIdx.x;
-    const int rb0 = blockIdx.y * kWaves;
-    const int nrb = min(kWaves, p.n_rb - rb0);
+    const int rb0 = (p.y0 + blockIdx.y) * kWaves;
+    const int nrb = kMode == kOneBlock ? 1 : kMode == kTwoGroups ? 2 : min(kWaves, p.n_rb - rb0);
     const int nkg = kWaves / nrb;
     const int my_rbl = wave % nrb;
     const int my_kg = wave / nrb;
@@ -671,9 +837,6 @@ void mla_split_kernel(Params p) {
     const int64_t ge = min(gs + chunk, total);
 
     const OperandOffsets offs = operand_offsets(lane);
-    // The waves' merge stats sit after the O rows of waves 2 and 3.
-    float *merge_m = reinterpret_cast<float *>(ring + kStageBytes) + 2 * kMergeWaveFloats;
-    float *merge_l = merge_m + kWaves * 16;
 
     int64_t base = 0;
     for (int b0 = 0; b0 < p.batch && base < ge; b0 += 64) {
@@ -718,7 +881,7 @@ void mla_split_kernel(Params p) {
             const int kgq = active ? my_kg : 0;
             const bool producer = active && my_rbl == 0;  // loads the keys of its group
             int kfirst, kstep, n_mine, n_iter = 0;
-            if (nrb == 1) {
+            if constexpr (!kShared) {
                 const int lim = min(seg_hi, vis_end);
                 const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
                 n_mine = nblk > my_kg ? (nblk - my_kg + nkg - 1) / nkg : 0;
@@ -736,23 +899,47 @@ void mla_split_kernel(Params p) {
             }
             // The first loads of the segment go out before the query is
             // fetched, so that the two round trips overlap.
-            char *const first = ring + (nrb == 1 ? wave : kgq * kPairSlots) * kBlockBytes;
-            if (producer && n_mine > 0) {
-                issue_block(first, bc, kfirst, page_of(bc, kfirst), lane);
-                if (nrb > 1) issue_block(first + kBlockBytes, bc, kfirst + kKeyBlock,
-                                         page_of(bc, kfirst + kKeyBlock), lane);
+            char *const first = stage0_base + (kShared ? kgq * kPairBytes : wave * kBlockBytes);  // not kOneGroup
+            // Lane byte offsets of the buffer-form loads (shared kernel).
+            int vrow[2];
+            {
+                const int r = lane >> 3;
+                const int w = (lane & 7) ^ row_swz(r);
+                vrow[0] = (r * kDqk + 8 * w) * 2;
+                vrow[1] = vrow[0] + 8 * kDqk * 2;
+            }
+            // Pages of the next step to issue (shared kernels).
+            int64_t pgA = 0, pgB = 0;
+            if constexpr (kMode == kOneBlock) {
+                if (n_mine > 0) issue_block(first, bc, kfirst, page_of(bc, kfirst), lane);
+            } else if constexpr (kMode == kTwoGroups) {
+                if (producer && n_mine > 0) {
+                    issue_block_buffer(first, bc, kfirst, page_of(bc, kfirst), vrow);
+                    issue_block_buffer(first + kBlockBytes, bc, kfirst + kKeyBlock, page_of(bc, kfirst + kKeyBlock),
+                                       vrow);
+                }
+                pgA = page_of(bc, kfirst + kstep);
+                pgB = page_of(bc, kfirst + kstep + kKeyBlock);
+            } else {
+                // Step 0, a quarter per wave.
+                if (n_mine > 0)
+                    issue_step_quarter(first, block_rsrc(bc, kfirst, page_of(bc, kfirst)),
+                                       block_rsrc(bc, kfirst + kKeyBlock, page_of(bc, kfirst + kKeyBlock)), vrow,
+                                       wave);
+                pgA = page_of(bc, kfirst + kstep);
+                pgB = page_of(bc, kfirst + kstep + kKeyBlock);
             }
             bf16x8 qf[kQkSteps];  // B operand Q^T: lane l -> head l%16, channels 32t + 8(l/16)
             if (active)
                 load_q(qf, p.q + (((int64_t)b * p.s_q + tok) * p.heads + h0 + (lane & 15)) * kDqk +
                                 8 * (lane >> 4));
 
-            if (nrb == 1) {
+            if constexpr (!kShared) {
                 // One row block: each wave streams its own blocks through a
                 // private two-stage ring, no barrier.
                 const int n_my = n_mine, step = kstep;
                 char *stage0 = first;
-                char *stage1 = first + kStageBytes;
+                char *stage1 = stage1_base + wave * kBlockBytes;
                 int64_t pg = page_of(bc, kfirst + step);  // pages are looked up a block ahead
                 int i = 0;
                 for (;;) {
@@ -788,87 +975,85 @@ void mla_split_kernel(Params p) {
                     ++i;
                 }
             } else {
-                // Several row blocks: the producer wave of each key group
-                // loads its steps into a shared ring of two; a barrier per
-                // step publishes it and frees the slots read one step ago,
-                // which then take the step after it.
+                // Several row blocks: the waves of each key group share each
+                // 32-key step of the group's keys.  The steps pass through a
+                // two-slot ring (step i in slot i % 2, each slot in an LDS
+                // array of its own); a barrier per step publishes it and
+                // frees the slot read one step ago, which then takes step
+                // i + 1.  Every wave of the group loads a share of each step
+                // (kOneGroup: all four waves a quarter, inactive ones too).
                 const int n_kg = n_mine, pstep = kstep;
                 const int key_end = min(vis_end, seg_hi);
-                char *slots = first;
-                // Pages are looked up one step ahead of their issue.
-                int64_t pgA = page_of(bc, kfirst + pstep), pgB = page_of(bc, kfirst + pstep + kKeyBlock);
-                auto issue_pair = [&](int pi) {
-                    char *dst = slots + (pi & 1) * 2 * kBlockBytes;
-                    const int kb = kfirst + pi * pstep;
-                    issue_block(dst, bc, kb, pgA, lane);
-                    issue_block(dst + kBlockBytes, bc, kb + kKeyBlock, pgB, lane);
-                    pgA = page_of(bc, kb + pstep);
-                    pgB = page_of(bc, kb + pstep + kKeyBlock);
-                };
-                int i = 0;
-                for (;;) {
-                    float sv[8], mx = -INFINITY;
-                    uint32_t vA[4] = {0, 0, 0, 0}, vB[4] = {0, 0, 0, 0};
-                    bool lagged = false;
-                    for (; i < n_iter; ++i) {
-                        if (producer) wait_vm<0>();  // step i landed (its only loads in flight)
-                        bare_barrier();  // step i is in; every wave is done with step i-1
-                        // Only now is step i-1's slot free for step i+1.
-                        if (producer && i + 1 < n_kg) issue_pair(i + 1);
-                        const int kb = kfirst + i * pstep;
-                        if (active && i < n_kg && kb < vis_end) {
-                            const char *stA = slots + (i & 1) * 2 * kBlockBytes;
-                            const char *stB = stA + kBlockBytes;
+                char *slots[2];
+                slots[0] = first;
+                slots[1] = stage1_base + kgq * kPairBytes;
+                // Step i with its slot fixed at compile time, so that every
+                // LDS access and direct load names its array.
+                PairReads rd;
+                rd.k_off[0] = offs.k_off[0];
+                rd.k_off[1] = offs.k_off[1];
 #pragma unroll
-                            for (int c4 = 0; c4 < 4; ++c4) {
-                                vA[c4] = (uint32_t)(uintptr_t)stA + offs.v_off[c4];
-                                vB[c4] = (uint32_t)(uintptr_t)stB + offs.v_off[c4];
-                            }
-                            pair_scores(sv, mx, stA, stB, offs.k_off, qf, kb, kb + kKeyBlock, key_end,
-                                        p.scale_log2, lane);
-                            if (__any(mx > ws.m + kMaxLag)) {
-                                lagged = true;
-                                break;
-                            }
-                            pair_pv(ws, sv, vA, vB);
-                        }
-                        wait_lgkm0();
+                for (int c4 = 0; c4 < 4; ++c4) rd.v_off[c4] = offs.v_off[c4];
+                auto step = [&](auto slot_idx, int i) {
+                    constexpr int P = decltype(slot_idx)::value;
+                    wait_vm<0>();    // this wave's share of step i landed
+                    bare_barrier();  // step i is in; every wave is done with step i-1
+                    // Only now is step i-1's slot free for step i + 1.
+                    if (i + 1 < n_kg && (kMode == kOneGroup || active)) {
+                        const int kb1 = kfirst + (i + 1) * pstep;
+                        if constexpr (kMode == kOneGroup)
+                            issue_step_quarter(slots[1 - P], block_rsrc(bc, kb1, pgA),
+                                               block_rsrc(bc, kb1 + kKeyBlock, pgB), vrow, wave);
+                        else
+                            issue_step_share(slots[1 - P], bc, kb1, pgA, pgB, vrow, my_rbl, nrb);
+                        pgA = page_of(bc, kb1 + pstep);
+                        pgB = page_of(bc, kb1 + pstep + kKeyBlock);
                     }
-                    if (!lagged) break;
-                    rescale(ws, mx);
-                    pair_pv(ws, sv, vA, vB);
+                    const int kb = kfirst + i * pstep;
+                    if (active && i < n_kg && kb < vis_end) {
+                        rd.stA = slots[P];
+                        rd.stB = rd.stA + kBlockBytes;
+                        float sv[8], mx;
+                        pair_scores(rd, sv, mx, qf, kb, key_end, p.scale_log2, lane);
+                        if (__any(mx > ws.m + kMaxLag)) rescale(ws, mx);  // rare
+                        pair_pv(rd, ws, sv);
+                    }
                     wait_lgkm0();
-                    ++i;
+                };
+                for (int i = 0; i < n_iter; i += 2) {
+                    step(Parity<0>{}, i);
+                    if (i + 1 < n_iter) step(Parity<1>{}, i + 1);
                 }
             }
 
-            // Merge the waves of this segment through LDS.
-            __syncthreads();
-            if (active) {
-                const int head = lane & 15;
-                const int grp = lane >> 4;
-                float lt = ws.l;
-                lt += __shfl_xor(lt, 16);
-                lt += __shfl_xor(lt, 32);
-                float *dst = merge_row_at(ring, wave, head) + 4 * grp;
+            if constexpr (kMode == kOneGroup) {
+                if (active) write_rows(p, ws, b, rb, whole, slot, lane);
+                bare_barrier();  // every wave is done with the ring before the next segment refills it
+            } else {
+                // Merge the waves of this segment through LDS.
+                __syncthreads();
+                if (active) {
+                    const int head = lane & 15;
+                    const int grp = lane >> 4;
+                    float lt = ws.l;
+                    lt += __shfl_xor(lt, 16);
+                    lt += __shfl_xor(lt, 32);
+                    float *dst = ma.row(wave, head) + 4 * grp;
 #pragma unroll
-                for (int ct = 0; ct < kOutTiles; ++ct)
-                    *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct];
-                if (grp == 0) {
-                    merge_m[wave * 16 + head] = ws.m;
-                    merge_l[wave * 16 + head] = lt;
+                    for (int ct = 0; ct < kOutTiles; ++ct)
+                        *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct];
+                    if (grp == 0) {
+                        ma.m[wave * 16 + head] = ws.m;
+                        ma.l[wave * 16 + head] = lt;
+                    }
                 }
-            }
-            __syncthreads();
-            for (int rbl = 0; rbl < nrb; ++rbl) {
-                if (nkg == 4)
-                    merge_waves<4>(p, ring, merge_m, merge_l, b, rb0, rbl, nrb, whole, slot);
-                else if (nkg == 2)
-                    merge_waves<2>(p, ring, merge_m, merge_l, b, rb0, rbl, nrb, whole, slot);
+                __syncthreads();
+                if constexpr (kMode == kOneBlock)
+                    merge_waves<4>(p, ma, b, rb0, 0, 1, whole, slot);
                 else
-                    merge_waves<1>(p, ring, merge_m, merge_l, b, rb0, rbl, nrb, whole, slot);
+                    for (int rbl = 0; rbl < nrb; ++rbl) merge_waves<2>(p, ma, b, rb0, rbl, nrb, whole, slot);
+                __syncthreads();
             }
-            __syncthreads();
         }
         base = next_base;
     }
@@ -1285,10 +1470,29 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t 
         }
     }
 
+    // Row-block groups of four (and a last group of three) run the one-group
+    // kernel, a last group of two the two-group one and a group of one
+    // (s_q * heads = 16, or the last group when n_rb % 4 == 1) the per-wave
+    // one.  Each launch covers groups y0 .. y0 + gridDim.y - 1.
+    const int rem = n_rb % kWaves;
+    const int full = n_rb / kWaves + (rem == 3 ? 1 : 0);
     LaunchTimer t_split(ctx, 0);
-    hipLaunchKernelGGL(mla_split_kernel, dim3(grid_x, n_rbg), dim3(kThreads), 0, ctx->stream, prm);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(ctx, e, "mla_split_kernel launch");
+    hipError_t e = hipSuccess;
+    if (full > 0) {
+        prm.y0 = 0;
+        hipLaunchKernelGGL(mla_split_kernel<kOneGroup>, dim3(grid_x, full), dim3(kThreads), 0, ctx->stream, prm);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(ctx, e, "mla_split_kernel launch");
+    }
+    if (rem == 1 || rem == 2) {
+        prm.y0 = n_rb / kWaves;
+        if (rem == 1)
+            hipLaunchKernelGGL(mla_split_kernel<kOneBlock>, dim3(grid_x, 1), dim3(kThreads), 0, ctx->stream, prm);
+        else
+            hipLaunchKernelGGL(mla_split_kernel<kTwoGroups>, dim3(grid_x, 1), dim3(kThreads), 0, ctx->stream, prm);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(ctx, e, "mla_split_kernel launch");
+    }
     t_split.done();
     if (need_combine) {
         LaunchTimer t_comb(ctx, 1);

@@ -58,6 +58,7 @@ SMALL = [
     (2, 1, 64, [257, 16], 16),
     (1, 4, 32, [129], 64),
     (4, 2, 48, [31, 32, 33, 500], 0),
+    (2, 5, 16, [7, 150], 16),           # row blocks 4 + 1: two kernels
 ]
 
 
@@ -138,6 +139,8 @@ MEDIUM = [
     (2, 3, 32, [4096, 4097], 256),
     (1, 4, 16, [65536], 0),
     (5, 1, 32, [1, 2, 3, 4, 5], 16),
+    (2, 1, 80, [2000, 33], 0),          # row blocks 4 + 1
+    (3, 3, 16, [1500, 3, 4000], 0),     # three row blocks sharing one key group
 ]
 
 

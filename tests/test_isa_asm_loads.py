@@ -27,8 +27,13 @@ def asm(tmp_path_factory):
     return out.read_text().split("\n")
 
 
-def split_kernel(asm):
-    start = next(i for i, l in enumerate(asm) if l.startswith("_ZN3mla16mla_split_kernelENS_6ParamsE:"))
+# Every instance of the split kernel: one row block per workgroup, two key
+# groups, one key group.
+SPLIT_KERNELS = tuple(f"_ZN3mla16mla_split_kernelILi{m}EEEvNS_6ParamsE" for m in range(3))
+
+
+def kernel_body(asm, name):
+    start = next(i for i, l in enumerate(asm) if l.startswith(name + ":"))
     end = next(i for i in range(start, len(asm)) if asm[i].strip().startswith("s_endpgm"))
     return asm[start:end + 1]
 
@@ -48,8 +53,9 @@ def asm_blocks(lines):
     return blocks
 
 
-def test_inline_asm_loads_wait_in_their_own_statement(asm):
-    blocks = asm_blocks(split_kernel(asm))
+@pytest.mark.parametrize("name", SPLIT_KERNELS)
+def test_inline_asm_loads_wait_in_their_own_statement(asm, name):
+    blocks = asm_blocks(kernel_body(asm, name))
     checked = 0
     for ins in blocks:
         lds = [i for i in ins if LDS_LOAD.match(i)]
@@ -69,7 +75,8 @@ def test_inline_asm_loads_wait_in_their_own_statement(asm):
     assert checked > 0, "no inline-asm loads found: the check is vacuous"
 
 
-def test_no_scratch_in_the_split_kernel(asm):
-    body = "\n".join(split_kernel(asm))
+@pytest.mark.parametrize("name", SPLIT_KERNELS)
+def test_no_scratch_in_the_split_kernel(asm, name):
+    body = "\n".join(kernel_body(asm, name))
     assert "scratch_" not in body, "the split kernel spills to scratch"
     assert "v_pk_mul_f32" not in body and "v_pk_add_f32" not in body and "v_pk_fma_f32" not in body

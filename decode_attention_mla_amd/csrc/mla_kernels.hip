@@ -301,7 +301,6 @@ __device__ inline void issue_block(char *stage, const BlockCtx &c, int kb, int64
 // makes every such wait a full one.  vrow[h] is the lane's byte offset of
 // its 16 bytes in rows 8h .. 8h+7 (row 8h + l/8, chunk (l%8) ^ swz(l/8)).
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit data format
-constexpr int kQuarter = 2 * kQkSteps / kWaves;  // loads per wave per step with one key group
 static_assert(kQkSteps * 1024 == kBlockBytes, "block B's slices follow block A's");
 template <int T>
 __device__ inline void buffer_load_slice(__amdgpu_buffer_rsrc_t rs, char *stage, const int (&vrow)[2]) {
@@ -315,7 +314,7 @@ __device__ inline void buffer_load_slices(__amdgpu_buffer_rsrc_t rs, char *stage
                                           std::integer_sequence<int, T...>) {
     (buffer_load_slice<T>(rs, stage, vrow), ...);
 }
-__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const BlockCtx &c, int kb, int64_t page);
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const BlockCtx &c, int kb, int64_t page, bool live = true);
 __device__ inline void issue_block_buffer(char *stage, const BlockCtx &c, int kb, int64_t page,
                                           const int (&vrow)[2]) {
     buffer_load_slices(block_rsrc(c, kb, page), stage, vrow, std::make_integer_sequence<int, kQkSteps>{});
@@ -325,15 +324,14 @@ __device__ inline void issue_block_buffer(char *stage, const BlockCtx &c, int kb
 // at kb + 16, in buffer form): slices share, share + nshare, ... of the
 // step's 36 (block A's 18, then block B's), so that the waves that compute
 // a step also split its loads.  block_rsrc: the descriptor of the block at
-// kb.  A block wholly past the last key (the second block of a sequence's
-// last step) gets an empty range: nothing is read and the stage fills with
-// zeros.  The descriptor must be wave-uniform (scalar registers);
+// kb.  A block wholly past the last key (or any block when !live) gets an
+// empty range: nothing is read and the stage fills with zeros.  The descriptor must be wave-uniform (scalar registers);
 // readfirstlane states it, else the compiler wraps every load in a
 // per-lane loop.
-__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const BlockCtx &c, int kb, int64_t page) {
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const BlockCtx &c, int kb, int64_t page, bool live) {
     const uint16_t *row0 = c.page_size ? c.kv + (page * c.page_size + kb % c.page_size) * (int64_t)kDqk
                                        : c.kv + (c.seq_base + kb) * (int64_t)kDqk;
-    const int rows = max(0, min(kKeyBlock, c.last_key + 1 - kb));
+    const int rows = live ? max(0, min(kKeyBlock, c.last_key + 1 - kb)) : 0;
     return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)uniform((int64_t)(uintptr_t)row0), 0,
                                              uniform(rows * kDqk * 2), kBufferWord3);
 }
@@ -352,23 +350,56 @@ __device__ inline void issue_step_share(char *dst, const BlockCtx &c, int kb, in
     }
 }
 
-// This wave's quarter of a step's loads (kOneGroup): slices share + 4k,
-// k < 9, of the step's 36 (block A's 18, then block B's), unrolled.
-__device__ inline void issue_step_quarter(char *dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                          const int (&vrow)[2], int share) {
-#pragma unroll
-    for (int k = 0; k < kQuarter; ++k) {
-        const int idx = share + kWaves * k;
-        const bool hb = idx >= kQkSteps;
-        const int t = hb ? idx - kQkSteps : idx;
-        // Slice t of block A or B sits at 1024 idx in the step's image (a
-        // plain offset, so the compiler still sees which array is written).
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb ? rb : ra,
-                                                 (__attribute__((address_space(3))) void *)(dst + 1024 * idx), 16,
-                                                 t < 9 ? vrow[0] : vrow[1], 128 * (t < 9 ? t : t - 9), 0,
-                                                 kNonTemporal);
+// One key group (kOneGroup) streams 64-key steps: four 16-key blocks, one
+// per wave to load (wave w: block w, its 18 slices).  The loads of step
+// i + 1 go out with the MFMAs of the first half of step i, one every
+// kQuadEvery: issued in a burst they would hold every wave until the memory
+// pipeline took them.
+constexpr int kQuadBlocks = kWaves;
+constexpr int kQuadBytes = kQuadBlocks * kBlockBytes;  // 72 KB
+constexpr int kQuadEvery = 5;
+static_assert(kQuadEvery * (kQkSteps - 1) < 2 * kQkSteps + 2 * kOutTiles, "within one pair's MFMAs");
+
+struct QuadLoads {
+    char *dst;                 // this wave's block in the step's slot
+    __amdgpu_buffer_rsrc_t r;  // that block's rows
+    int vrow[2];
+
+    template <int T>
+    __device__ void slice() {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + T * 1024), 16,
+                                                 vrow[T / 9], 128 * (T % 9), 0, kNonTemporal);
     }
-}
+    template <int... T>
+    __device__ void all(std::integer_sequence<int, T...>) {
+        (slice<T>(), ...);
+    }
+    // The load that goes with MFMA g of the pair, if any.
+    __device__ void operator()(int g) {
+        if (g % kQuadEvery != 0 || g / kQuadEvery >= kQkSteps) return;
+        switch (g / kQuadEvery) {  // compile-time after unrolling
+        case 0: slice<0>(); break;
+        case 1: slice<1>(); break;
+        case 2: slice<2>(); break;
+        case 3: slice<3>(); break;
+        case 4: slice<4>(); break;
+        case 5: slice<5>(); break;
+        case 6: slice<6>(); break;
+        case 7: slice<7>(); break;
+        case 8: slice<8>(); break;
+        case 9: slice<9>(); break;
+        case 10: slice<10>(); break;
+        case 11: slice<11>(); break;
+        case 12: slice<12>(); break;
+        case 13: slice<13>(); break;
+        case 14: slice<14>(); break;
+        case 15: slice<15>(); break;
+        case 16: slice<16>(); break;
+        default: slice<17>(); break;
+        }
+    }
+};
+static_assert(kQkSteps == 18, "QuadLoads lists the 18 slices of a block");
 
 // Per-lane byte offsets of the operand reads within a block image.
 //  K operand of QK^T step t (lane l -> key k = l%16, chunk 4t + l/16):
@@ -592,6 +623,12 @@ constexpr int kAhead = 12;
 static_assert(kAhead <= kPairK, "the stream starts with K reads");
 
 
+// Work issued with the MFMAs of a 32-key pair: side(g) runs after MFMA g
+// (g = 0 .. 99: the 36 QK^T MFMAs, then the 64 PV ones).
+struct NoSide {
+    __device__ void operator()(int) const {}
+};
+
 struct PairReads {
     const char *stA, *stB;  // the step's blocks A and B
     int k_off[2];
@@ -615,8 +652,9 @@ struct PairReads {
 // (sv[i]) and of block B (sv[4 + i]), scaled into the log2 domain and
 // masked; mx is their max over the head.  Leaves the first kAhead V^T reads
 // of the stream in flight.
+template <typename Side = NoSide>
 __device__ inline void pair_scores(PairReads &rd, float (&sv)[8], float &mx, const bf16x8 (&qf)[kQkSteps],
-                                   int kbA, int key_end, float scale_log2, int lane) {
+                                   int kbA, int key_end, float scale_log2, int lane, Side side = Side{}) {
 #pragma unroll
     for (int r = 0; r < kAhead; ++r) rd.read(r);
     __builtin_amdgcn_sched_barrier(0);
@@ -626,6 +664,7 @@ __device__ inline void pair_scores(PairReads &rd, float (&sv)[8], float &mx, con
         const int h = n / kQkSteps, t = n % kQkSteps;
         s[h][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rd.ka[n], qf[t], s[h][t & 1], 0, 0, 0);
         rd.read(n + kAhead);
+        side(n);
         __builtin_amdgcn_sched_barrier(0);
     }
     const int kA = kbA + 4 * (lane >> 4), kB = kA + kKeyBlock;
@@ -647,7 +686,8 @@ __device__ inline void pair_scores(PairReads &rd, float (&sv)[8], float &mx, con
 // hi and lo halves (two MFMAs per tile), and V^T (A operand) joins one
 // transposing read of each block.  Within a group of four tiles the hi
 // MFMAs come before the lo ones, so no MFMA waits on the one before it.
-__device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8]) {
+template <typename Side = NoSide>
+__device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8], Side side = Side{}) {
     bf16x8 phi, plo;
     float psum = 0.f;
 #pragma unroll
@@ -667,6 +707,7 @@ __device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8
             bf16x8, __builtin_shufflevector(rd.vr[2 * ct], rd.vr[2 * ct + 1], 0, 1, 2, 3, 4, 5, 6, 7));
         ws.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (m & 4) ? plo : phi, ws.acc[ct], 0, 0, 0);
         rd.read(kPairK + kAhead + m);
+        side(kPairK + m);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -776,11 +817,10 @@ __device__ inline void write_rows(const Params &p, const WaveState &ws, int b, i
 //              private two-stage ring, no barrier.
 //  kTwoGroups  nrb = 2: two key groups of two waves; the waves of a group
 //              share each 32-key step through a two-slot ring.
-//  kOneGroup   nrb = 3, 4: one key group of four waves sharing each 32-key
+//  kOneGroup   nrb = 3, 4: one key group of four waves sharing each 64-key
 //              step through a two-slot ring; all four waves issue a quarter
 //              of each step's loads, and each wave writes its rows itself.
 enum SplitMode { kOneBlock = 0, kTwoGroups = 1, kOneGroup = 2 };
-constexpr int kOneGroupSlot = kPairBytes;  // 36 KB: one step
 
 template <int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -793,8 +833,8 @@ void mla_split_kernel(Params p) {
         // accesses of distinct arrays apart, so its own reads of one slot
         // never wait for direct loads still landing in the other.  (Each
         // wave writes its rows itself: no merge area.)
-        __shared__ __attribute__((aligned(16))) char slot_a[kOneGroupSlot];
-        __shared__ __attribute__((aligned(16))) char slot_b[kOneGroupSlot];
+        __shared__ __attribute__((aligned(16))) char slot_a[kQuadBytes];
+        __shared__ __attribute__((aligned(16))) char slot_b[kQuadBytes];
         stage0_base = slot_a;
         stage1_base = slot_b;
     } else {
@@ -887,6 +927,13 @@ void mla_split_kernel(Params p) {
                 n_mine = nblk > my_kg ? (nblk - my_kg + nkg - 1) / nkg : 0;
                 kstep = kKeyBlock * nkg;
                 kfirst = seg_lo + kKeyBlock * my_kg;
+            } else if constexpr (kMode == kOneGroup) {
+                const int tok_last = (rb0 + nrb - 1) / hpt;  // sees the most keys
+                const int lim = min(seg_hi, L - p.s_q + tok_last + 1);
+                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
+                n_iter = n_mine = (nblk + kQuadBlocks - 1) / kQuadBlocks;
+                kstep = kQuadBlocks * kKeyBlock;
+                kfirst = seg_lo;
             } else {
                 const int tok_last = (rb0 + nrb - 1) / hpt;  // sees the most keys
                 const int lim = min(seg_hi, L - p.s_q + tok_last + 1);
@@ -908,7 +955,8 @@ void mla_split_kernel(Params p) {
                 vrow[0] = (r * kDqk + 8 * w) * 2;
                 vrow[1] = vrow[0] + 8 * kDqk * 2;
             }
-            // Pages of the next step to issue (shared kernels).
+            // Pages of the next step to issue (shared kernels; kOneGroup: this
+            // wave's block in pgA).
             int64_t pgA = 0, pgB = 0;
             if constexpr (kMode == kOneBlock) {
                 if (n_mine > 0) issue_block(first, bc, kfirst, page_of(bc, kfirst), lane);
@@ -922,12 +970,16 @@ void mla_split_kernel(Params p) {
                 pgB = page_of(bc, kfirst + kstep + kKeyBlock);
             } else {
                 // Step 0, a quarter per wave.
-                if (n_mine > 0)
-                    issue_step_quarter(first, block_rsrc(bc, kfirst, page_of(bc, kfirst)),
-                                       block_rsrc(bc, kfirst + kKeyBlock, page_of(bc, kfirst + kKeyBlock)), vrow,
-                                       wave);
-                pgA = page_of(bc, kfirst + kstep);
-                pgB = page_of(bc, kfirst + kstep + kKeyBlock);
+                if (n_mine > 0) {
+                    const int kbw = kfirst + wave * kKeyBlock;  // this wave's block
+                    QuadLoads q0;
+                    q0.dst = first + wave * kBlockBytes;
+                    q0.r = block_rsrc(bc, kbw, page_of(bc, kbw));
+                    q0.vrow[0] = vrow[0];
+                    q0.vrow[1] = vrow[1];
+                    q0.all(std::make_integer_sequence<int, kQkSteps>{});
+                }
+                pgA = page_of(bc, kfirst + kstep + wave * kKeyBlock);
             }
             bf16x8 qf[kQkSteps];  // B operand Q^T: lane l -> head l%16, channels 32t + 8(l/16)
             if (active)
@@ -975,13 +1027,15 @@ void mla_split_kernel(Params p) {
                     ++i;
                 }
             } else {
-                // Several row blocks: the waves of each key group share each
-                // 32-key step of the group's keys.  The steps pass through a
-                // two-slot ring (step i in slot i % 2, each slot in an LDS
-                // array of its own); a barrier per step publishes it and
+                // Several row blocks share each step of keys, which passes
+                // through a two-slot ring (step i in slot i % 2, each slot an
+                // LDS array of its own); a barrier per step publishes it and
                 // frees the slot read one step ago, which then takes step
-                // i + 1.  Every wave of the group loads a share of each step
-                // (kOneGroup: all four waves a quarter, inactive ones too).
+                // i + 1.  kTwoGroups: each key group's two waves share 32-key
+                // steps and split their loads at the barrier.  kOneGroup: the
+                // four waves share 64-key steps (two 32-key pairs), and every
+                // wave, inactive ones too, issues a quarter of the next
+                // step's loads with the MFMAs of the first pair.
                 const int n_kg = n_mine, pstep = kstep;
                 const int key_end = min(vis_end, seg_hi);
                 char *slots[2];
@@ -994,29 +1048,44 @@ void mla_split_kernel(Params p) {
                 rd.k_off[1] = offs.k_off[1];
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4) rd.v_off[c4] = offs.v_off[c4];
-                auto step = [&](auto slot_idx, int i) {
+                // One 32-key pair: blocks at `blocks` and blocks + 18 KB, keys kbp .. kbp + 31.
+                auto pair = [&](const char *blocks, int kbp, auto side) __attribute__((always_inline)) {
+                    rd.stA = blocks;
+                    rd.stB = blocks + kBlockBytes;
+                    float sv[8], mx;
+                    pair_scores(rd, sv, mx, qf, kbp, key_end, p.scale_log2, lane, side);
+                    if (__any(mx > ws.m + kMaxLag)) rescale(ws, mx);  // rare
+                    pair_pv(rd, ws, sv, side);
+                };
+                auto step = [&](auto slot_idx, int i) __attribute__((always_inline)) {
                     constexpr int P = decltype(slot_idx)::value;
                     wait_vm<0>();    // this wave's share of step i landed
                     bare_barrier();  // step i is in; every wave is done with step i-1
                     // Only now is step i-1's slot free for step i + 1.
-                    if (i + 1 < n_kg && (kMode == kOneGroup || active)) {
-                        const int kb1 = kfirst + (i + 1) * pstep;
-                        if constexpr (kMode == kOneGroup)
-                            issue_step_quarter(slots[1 - P], block_rsrc(bc, kb1, pgA),
-                                               block_rsrc(bc, kb1 + kKeyBlock, pgB), vrow, wave);
-                        else
-                            issue_step_share(slots[1 - P], bc, kb1, pgA, pgB, vrow, my_rbl, nrb);
-                        pgA = page_of(bc, kb1 + pstep);
-                        pgB = page_of(bc, kb1 + pstep + kKeyBlock);
-                    }
                     const int kb = kfirst + i * pstep;
-                    if (active && i < n_kg && kb < vis_end) {
-                        rd.stA = slots[P];
-                        rd.stB = rd.stA + kBlockBytes;
-                        float sv[8], mx;
-                        pair_scores(rd, sv, mx, qf, kb, key_end, p.scale_log2, lane);
-                        if (__any(mx > ws.m + kMaxLag)) rescale(ws, mx);  // rare
-                        pair_pv(rd, ws, sv);
+                    if constexpr (kMode == kOneGroup) {
+                        // Step i + 1's loads (empty ranges past the last
+                        // step: the count stays fixed inside the MFMA stream).
+                        const int kbw = kb + pstep + wave * kKeyBlock;  // this wave's block of step i + 1
+                        QuadLoads ql;
+                        ql.dst = slots[1 - P] + wave * kBlockBytes;
+                        ql.r = block_rsrc(bc, kbw, pgA, i + 1 < n_kg);
+                        ql.vrow[0] = vrow[0];
+                        ql.vrow[1] = vrow[1];
+                        pgA = page_of(bc, kbw + pstep);
+                        if (active && kb < vis_end)
+                            pair(slots[P], kb, ql);
+                        else
+                            ql.all(std::make_integer_sequence<int, kQkSteps>{});
+                        if (active && kb + 2 * kKeyBlock < vis_end)
+                            pair(slots[P] + 2 * kBlockBytes, kb + 2 * kKeyBlock, NoSide{});
+                    } else {
+                        if (active && i + 1 < n_kg) {
+                            issue_step_share(slots[1 - P], bc, kb + pstep, pgA, pgB, vrow, my_rbl, nrb);
+                            pgA = page_of(bc, kb + 2 * pstep);
+                            pgB = page_of(bc, kb + 2 * pstep + kKeyBlock);
+                        }
+                        if (active && i < n_kg && kb < vis_end) pair(slots[P], kb, NoSide{});
                     }
                     wait_lgkm0();
                 };
@@ -1028,7 +1097,11 @@ void mla_split_kernel(Params p) {
 
             if constexpr (kMode == kOneGroup) {
                 if (active) write_rows(p, ws, b, rb, whole, slot, lane);
-                bare_barrier();  // every wave is done with the ring before the next segment refills it
+                // Every wave is done with the ring, and every load into it
+                // (the empty ones past the last step included) has landed,
+                // before the next segment refills it.
+                wait_vm<0>();
+                bare_barrier();
             } else {
                 // Merge the waves of this segment through LDS.
                 __syncthreads();

@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV HBM GB/s (% of peak) + µs/call, MLA decode bs16 ctx64K 16 heads"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("decode_attention_mla_amd/csrc/mla_kernels.hip",
+KERNEL_SOURCES = ("decode_attention_mla_amd/csrc/mla_kernels.hip", "decode_attention_mla_amd/csrc/context.h",
                   "decode_attention_mla_amd/csrc/plan.h", "include/mla_decode.h")
 
 

@@ -86,9 +86,13 @@ def load() -> ctypes.CDLL:
                              ctypes.POINTER(i32), ctypes.POINTER(PlanInfo)]
     lib.mla_ctx_kernel_times.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.mla_append_kv.argtypes = [P, P, P, P, P, ctypes.POINTER(Problem)]
+    lib.mla_absorb_q.argtypes = [P, P, P, P, P, i32, i32, i32]
+    lib.mla_project_out.argtypes = [P, P, P, P, i32, i32, i32]
     lib.mla_version.restype = ctypes.c_char_p
     for name in ("mla_ctx_create", "mla_ctx_destroy", "mla_ctx_reserve", "mla_ctx_set_option",
-                 "mla_decode", "mla_validate", "mla_plan", "mla_ctx_kernel_times"):
+                 "mla_decode", "mla_validate", "mla_plan", "mla_ctx_kernel_times",
+                 "mla_append_kv", "mla_absorb_q", "mla_project_out"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -216,3 +220,87 @@ def mla_decode(ctx: Context, q, kv_cache, block_table, seqlens, scale: float, ou
     del keep
     _check(rc, ctx.handle)
     return out, lse
+
+
+def _need(name, t, dtype, ndim=None):
+    import torch
+
+    if t.dtype != dtype or not t.is_contiguous() or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise TypeError(f"{name} must have {ndim} dimensions, has {t.dim()}")
+
+
+def mla_append_kv(ctx: Context, new_rows, kv_cache, block_table, seqlens,
+                  seqlens_host: Optional[np.ndarray] = None, kv_capacity: Optional[int] = None):
+    """Write the latent rows of the new tokens into the cache, in place.
+
+    new_rows [B, s_q, 576] bf16; kv_cache, block_table and seqlens as for
+    ``mla_decode`` (seqlens are the lengths including the new tokens).
+    Returns kv_cache.
+    """
+    import torch
+
+    _need("new_rows", new_rows, torch.bfloat16, 3)
+    _need("kv_cache", kv_cache, torch.bfloat16, 3)
+    _need("seqlens", seqlens, torch.int32, 1)
+    B, s_q, dqk = new_rows.shape
+    if block_table is None:
+        page_size, num_pages, max_pages, bt_ptr = 0, 0, 0, None
+        cap = kv_cache.shape[1] if kv_capacity is None else kv_capacity
+    else:
+        _need("block_table", block_table, torch.int32, 2)
+        page_size, num_pages, max_pages = kv_cache.shape[1], kv_cache.shape[0], block_table.shape[1]
+        cap, bt_ptr = 0, block_table.data_ptr()
+    pr, keep = make_problem(B, s_q, 1, page_size, cap, num_pages, max_pages, seqlens_host)
+    pr.head_dim_qk = dqk
+    rc = load().mla_append_kv(ctx.handle, new_rows.data_ptr(), kv_cache.data_ptr(), bt_ptr,
+                              seqlens.data_ptr(), ctypes.byref(pr))
+    del keep
+    _check(rc, ctx.handle)
+    return kv_cache
+
+
+def mla_absorb_q(ctx: Context, q_nope, q_rope, w_uk, q_out=None):
+    """Absorbed query [..., H, 576] bf16 from q_nope [..., H, d_nope],
+    q_rope [..., H, 64] (bf16) and w_uk [H, 512, d_nope] bf16."""
+    import torch
+
+    _need("q_nope", q_nope, torch.bfloat16)
+    _need("q_rope", q_rope, torch.bfloat16)
+    _need("w_uk", w_uk, torch.bfloat16, 3)
+    H, lat, d_nope = w_uk.shape
+    lead = q_nope.shape[:-2]
+    if q_nope.shape[-2:] != (H, d_nope) or q_rope.shape != (*lead, H, HEAD_DIM_QK - HEAD_DIM_V):
+        raise TypeError("q_nope / q_rope shapes do not match w_uk")
+    rows = int(np.prod(lead)) if len(lead) else 1
+    if q_out is None:
+        q_out = torch.empty((*lead, H, HEAD_DIM_QK), dtype=torch.bfloat16, device=q_nope.device)
+    _need("q_out", q_out, torch.bfloat16)
+    if q_out.numel() != rows * H * HEAD_DIM_QK:
+        raise TypeError("q_out has the wrong size")
+    _check(load().mla_absorb_q(ctx.handle, q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(),
+                               q_out.data_ptr(), rows, H, d_nope), ctx.handle)
+    return q_out
+
+
+def mla_project_out(ctx: Context, o, w_uv, out=None):
+    """Output up-projection [..., H, d_v] fp32 from the latent attention
+    output o [..., H, 512] fp32 and w_uv [H, d_v, 512] bf16."""
+    import torch
+
+    _need("o", o, torch.float32)
+    _need("w_uv", w_uv, torch.bfloat16, 3)
+    H, d_v, lat = w_uv.shape
+    lead = o.shape[:-2]
+    if o.shape[-2:] != (H, lat):
+        raise TypeError("o shape does not match w_uv")
+    rows = int(np.prod(lead)) if len(lead) else 1
+    if out is None:
+        out = torch.empty((*lead, H, d_v), dtype=torch.float32, device=o.device)
+    _need("out", out, torch.float32)
+    if out.numel() != rows * H * d_v:
+        raise TypeError("out has the wrong size")
+    _check(load().mla_project_out(ctx.handle, o.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
+                                  rows, H, d_v), ctx.handle)
+    return out

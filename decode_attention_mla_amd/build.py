@@ -1,7 +1,8 @@
 """Build the gfx950 MLA decode library in-tree with hipcc.
 
 ``python -m decode_attention_mla_amd.build`` (or ``build()``) always
-recompiles ``csrc/mla_kernels.hip`` into ``_lib/libmla_decode.so``.
+recompiles ``csrc/mla_kernels.hip`` and ``csrc/mla_steps.hip`` into
+``_lib/libmla_decode.so``.
 """
 from __future__ import annotations
 
@@ -11,7 +12,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "mla_kernels.hip")
+SRC = os.path.join(PKG, "csrc", "mla_kernels.hip")         # the attention kernels
+SRCS = [SRC, os.path.join(PKG, "csrc", "mla_steps.hip")]  # every source of the library
 LIB = os.path.join(PKG, "_lib", "libmla_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -34,7 +36,7 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

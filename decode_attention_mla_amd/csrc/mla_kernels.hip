@@ -52,6 +52,7 @@
 #include <utility>
 #include <vector>
 
+#include "context.h"
 #include "mla_decode.h"
 #include "plan.h"
 
@@ -1207,44 +1208,10 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
 
 // =================================================================== host side
 
-struct mla_ctx {
-    hipStream_t stream = nullptr;
-    int device = 0;
-    int cu_count = 256;
-    int64_t opt_splits = 0;
-    int64_t opt_min_chunk = mla::kDefaultMinChunk;
-    bool timing = false;
-    void *ws = nullptr;
-    size_t ws_bytes = 0;
-    std::string err;
-    // Event pairs around recorded launches: kind 0 = split, 1 = combine.
-    struct Timed {
-        hipEvent_t start, stop;
-        int kind;
-    };
-    std::vector<Timed> timed;
-    std::vector<hipEvent_t> spare;
-};
-
 namespace {
 
-thread_local std::string g_err;
-
-int fail(mla_ctx *ctx, int code, const char *fmt, ...) __attribute__((format(printf, 3, 4)));
-int fail(mla_ctx *ctx, int code, const char *fmt, ...) {
-    char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
-    if (ctx) ctx->err = buf;
-    else g_err = buf;
-    return code;
-}
-
-int hip_fail(mla_ctx *ctx, hipError_t e, const char *what) {
-    return fail(ctx, MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
-}
+using mla_host::fail;
+using mla_host::hip_fail;
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
@@ -1307,19 +1274,19 @@ extern "C" {
 
 const char *mla_version(void) { return "mla_decode 0.1 gfx950"; }
 
-const char *mla_last_error(const mla_ctx *ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+const char *mla_last_error(const mla_ctx *ctx) { return ctx ? ctx->err.c_str() : mla_host::thread_error().c_str(); }
 
 int mla_validate(const void *q, const void *kv_cache, const int32_t *block_table,
                  const int32_t *seqlens, float scale, const float *out, const float *lse,
                  const mla_problem *p) {
-    g_err.clear();
+    mla_host::thread_error().clear();
     return check(nullptr, q, kv_cache, block_table, seqlens, scale, out, lse, p);
 }
 
 int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits, int64_t min_chunk,
              mla_plan_segment *segs, int32_t max_segs, int32_t *n_segs, mla_plan_info *info) {
     using namespace mla;
-    g_err.clear();
+    mla_host::thread_error().clear();
     if (!seqlens_host || batch < 1 || num_splits < 1 || !n_segs)
         return fail(nullptr, MLA_ERR_INVALID_ARG, "mla_plan: bad arguments");
     int64_t total = 0;
@@ -1360,7 +1327,7 @@ int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits, int
 }
 
 int mla_ctx_create(mla_ctx **out_ctx, void *stream) {
-    g_err.clear();
+    mla_host::thread_error().clear();
     if (!out_ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx out-pointer is NULL");
     *out_ctx = nullptr;
     int dev = 0;

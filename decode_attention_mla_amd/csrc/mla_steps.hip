@@ -1,0 +1,286 @@
+// The MLA steps on either side of the attention kernel, for MI355X (gfx950).
+//
+// MLA keeps one latent row per token: the low-rank joint compression of the
+// keys and values ("FlashMLA-ETAP", gist.science technical summary,
+// Integration and Implementation).  Read as 512 compressed-KV channels and
+// a 64-channel rotary key, the row lets each head's key up-projection be
+// folded into its query (the absorbed query), and the value up-projection
+// be applied once to the attention output:
+//   * append:  the new tokens' latent rows go into the cache;
+//   * absorb:  q[h] = [ W_UK[h]^T q_nope[h] , q_rope[h] ]  (576 wide, bf16);
+//   * project: out[h] = W_UV[h] o[h]  (o: the 512-wide latent output).
+//
+// At decode sizes (a few to a few hundred query rows) the projections read
+// each weight once and do 2 x rows flops per weight: they are bound by the
+// weights' HBM bytes up to rows ~ 150, so the kernels below aim at plain
+// coalesced streaming with MFMA doing the arithmetic, not at data reuse.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "context.h"
+#include "mla_decode.h"
+
+namespace mla_steps {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+constexpr int kLatent = MLA_HEAD_DIM_V;                // 512 compressed channels
+constexpr int kRope = MLA_HEAD_DIM_QK - MLA_HEAD_DIM_V;  // 64 rotary channels
+constexpr int kRowBytes = MLA_HEAD_DIM_QK * 2;          // 1152
+constexpr int kTileCh = 64;                             // output channels per wave (4 MFMA tiles)
+
+struct AppendParams {
+    const uint16_t *rows;  // [B][s_q][576]
+    uint16_t *kv;
+    const int32_t *block_table;
+    const int32_t *seqlens;
+    int64_t kv_capacity;   // contiguous
+    int64_t num_pages;     // paged
+    int64_t capacity;      // keys one sequence can hold
+    int32_t s_q;
+    int32_t page_size;
+    int32_t max_pages;
+};
+
+// One wave per new row: 72 chunks of 16 bytes.
+__global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
+    const int row = blockIdx.x;  // b * s_q + t
+    const int b = row / p.s_q, t = row % p.s_q;
+    int64_t L = p.seqlens[b];
+    L = L < p.s_q ? p.s_q : (L > p.capacity ? p.capacity : L);
+    const int64_t key = L - p.s_q + t;
+    int64_t dst_row;
+    if (p.page_size) {
+        int64_t page = p.block_table[(int64_t)b * p.max_pages + key / p.page_size];
+        page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+        dst_row = page * p.page_size + key % p.page_size;
+    } else {
+        dst_row = (int64_t)b * p.kv_capacity + key;
+    }
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(p.rows + (int64_t)row * MLA_HEAD_DIM_QK);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(p.kv + dst_row * MLA_HEAD_DIM_QK);
+    for (int c = threadIdx.x; c < kRowBytes / 16; c += 64) dst[c] = src[c];
+}
+
+// The B operand of a 16x16x32 MFMA (or the A operand, same layout) for row
+// block `r0`: lane l gets 8 consecutive bf16 of row r0 + l%16 at column
+// 8(l/16) + k0, or zeros past the last row.
+__device__ inline bf16x8 load_rows8(const uint16_t *base, int64_t row_stride, int r0, int rows, int k0,
+                                    int lane) {
+    const int r = r0 + (lane & 15);
+    if (r >= rows) return bf16x8{};
+    return *reinterpret_cast<const bf16x8 *>(base + (int64_t)r * row_stride + k0 + 8 * (lane >> 4));
+}
+
+struct AbsorbParams {
+    const uint16_t *q_nope;  // [rows][H][d_nope]
+    const uint16_t *q_rope;  // [rows][H][64]
+    const uint16_t *w_uk;    // [H][512][d_nope]
+    uint16_t *q_out;         // [rows][H][576]
+    int32_t rows, heads, d_nope;
+};
+
+// Wave (cg, h, rt): latent channels 64cg .. 64cg+63 of head h for rows
+// 16rt .. 16rt+15.  q_lat^T (channels x rows) = W_UK[h] (channels x d_nope)
+// . q_nope^T (d_nope x rows): A from the weight rows, B from the query rows,
+// both 16 contiguous bytes per lane; D lane l: row l%16, channels
+// 16ct + 4(l/16) .. +3, stored as 4 bf16.  The wave of channel group 0 also
+// copies the rotary part of its rows.
+__global__ __launch_bounds__(64) void absorb_kernel(AbsorbParams p) {
+    const int lane = threadIdx.x;
+    const int cg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16;
+    const int64_t q_stride = (int64_t)p.heads * p.d_nope;  // between rows
+    const uint16_t *qn = p.q_nope + (int64_t)h * p.d_nope;
+    const uint16_t *w = p.w_uk + ((int64_t)h * kLatent + cg * kTileCh) * p.d_nope;
+    f32x4 acc[4] = {};
+    for (int k0 = 0; k0 < p.d_nope; k0 += 32) {
+        const bf16x8 bq = load_rows8(qn, q_stride, r0, p.rows, k0, lane);
+        bf16x8 aw[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) aw[ct] = load_rows8(w + ct * 16 * p.d_nope, p.d_nope, 0, 16, k0, lane);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ct], bq, acc[ct], 0, 0, 0);
+    }
+    const int r = r0 + (lane & 15);
+    if (r < p.rows) {
+        uint16_t *out = p.q_out + ((int64_t)r * p.heads + h) * MLA_HEAD_DIM_QK + cg * kTileCh + 4 * (lane >> 4);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(acc[ct][i]);  // to nearest even
+            *reinterpret_cast<bf16x4 *>(out + 16 * ct) = v;
+        }
+    }
+    if (cg == 0) {
+        // Rotary part: 16 rows x 128 B, lane l -> row l/4, 32 bytes.
+        const int rr = r0 + (lane >> 2);
+        if (rr < p.rows) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(p.q_rope + ((int64_t)rr * p.heads + h) * kRope) +
+                               2 * (lane & 3);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(p.q_out + ((int64_t)rr * p.heads + h) * MLA_HEAD_DIM_QK + kLatent) +
+                         2 * (lane & 3);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        }
+    }
+}
+
+struct ProjectParams {
+    const float *o;         // [rows][H][512]
+    const uint16_t *w_uv;   // [H][d_v][512]
+    float *out;             // [rows][H][d_v]
+    int32_t rows, heads, d_v;
+};
+
+// Wave (eg, h, rt): value channels 64eg .. 64eg+63 of head h for rows
+// 16rt .. 16rt+15.  out^T (d_v x rows) = W_UV[h] (d_v x 512) . o^T
+// (512 x rows): A from the weight rows, B from the output rows split into
+// bf16 hi + lo (two MFMAs per k step); D lane l: row l%16, channels
+// 16ct + 4(l/16) .. +3, stored as 16 bytes.
+__global__ __launch_bounds__(64) void project_kernel(ProjectParams p) {
+    const int lane = threadIdx.x;
+    const int eg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16;
+    const int r = r0 + (lane & 15);
+    const bool live = r < p.rows;
+    const float *orow = p.o + ((int64_t)r * p.heads + h) * kLatent + 8 * (lane >> 4);
+    const uint16_t *w = p.w_uv + ((int64_t)h * p.d_v + eg * kTileCh) * kLatent;
+    f32x4 acc[4] = {};
+    for (int k0 = 0; k0 < kLatent; k0 += 32) {
+        f32x4 x0 = {}, x1 = {};
+        if (live) {
+            x0 = *reinterpret_cast<const f32x4 *>(orow + k0);
+            x1 = *reinterpret_cast<const f32x4 *>(orow + k0 + 4);
+        }
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = j < 4 ? x0[j] : x1[j - 4];
+            const __bf16 hb = static_cast<__bf16>(x);
+            hi[j] = hb;
+            lo[j] = static_cast<__bf16>(x - static_cast<float>(hb));
+        }
+        bf16x8 aw[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) aw[ct] = load_rows8(w + ct * 16 * kLatent, kLatent, 0, 16, k0, lane);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ct], hi, acc[ct], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ct], lo, acc[ct], 0, 0, 0);
+    }
+    if (live) {
+        float *out = p.out + ((int64_t)r * p.heads + h) * p.d_v + eg * kTileCh + 4 * (lane >> 4);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) *reinterpret_cast<f32x4 *>(out + 16 * ct) = acc[ct];
+    }
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+}  // namespace mla_steps
+
+using mla_host::fail;
+using mla_host::hip_fail;
+
+extern "C" {
+
+int mla_append_kv(mla_ctx *ctx, const void *new_rows, void *kv_cache, const int32_t *block_table,
+                  const int32_t *seqlens, const mla_problem *p) {
+    using namespace mla_steps;
+    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->err.clear();
+    if (!p) return fail(ctx, MLA_ERR_INVALID_ARG, "problem description is NULL");
+    if (!new_rows || !kv_cache || !seqlens)
+        return fail(ctx, MLA_ERR_INVALID_ARG, "new_rows, kv_cache and seqlens must be non-NULL");
+    if (p->batch < 1 || p->s_q < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "batch and s_q must be >= 1");
+    if ((int64_t)p->batch * p->s_q > INT32_MAX) return fail(ctx, MLA_ERR_UNSUPPORTED, "batch * s_q too large");
+    if (p->head_dim_qk != MLA_HEAD_DIM_QK)
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "head_dim_qk must be %d (got %d)", MLA_HEAD_DIM_QK, p->head_dim_qk);
+    if (!aligned16(new_rows) || !aligned16(kv_cache))
+        return fail(ctx, MLA_ERR_INVALID_ARG, "new_rows and kv_cache must be 16-byte aligned");
+    AppendParams ap{};
+    ap.rows = static_cast<const uint16_t *>(new_rows);
+    ap.kv = static_cast<uint16_t *>(kv_cache);
+    ap.seqlens = seqlens;
+    ap.s_q = p->s_q;
+    if (p->page_size == 0) {
+        if (block_table)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "block_table given but page_size is 0 (contiguous)");
+        if (p->kv_capacity < p->s_q || p->kv_capacity > (int64_t)INT32_MAX)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "kv_capacity must be in [s_q, 2^31) (got %lld)",
+                        (long long)p->kv_capacity);
+        ap.kv_capacity = p->kv_capacity;
+        ap.capacity = p->kv_capacity;
+    } else {
+        if (p->page_size < 0 || p->page_size % MLA_KEY_BLOCK)
+            return fail(ctx, MLA_ERR_UNSUPPORTED, "page_size must be a positive multiple of %d (got %d)",
+                        MLA_KEY_BLOCK, p->page_size);
+        if (!block_table) return fail(ctx, MLA_ERR_INVALID_ARG, "paged layout needs a block_table");
+        if (p->num_pages < 1 || p->max_pages < 1)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
+        ap.capacity = (int64_t)p->max_pages * p->page_size;
+        if (ap.capacity < p->s_q || ap.capacity > (int64_t)INT32_MAX)
+            return fail(ctx, MLA_ERR_INVALID_ARG, "max_pages * page_size must be in [s_q, 2^31)");
+        ap.block_table = block_table;
+        ap.page_size = p->page_size;
+        ap.num_pages = p->num_pages;
+        ap.max_pages = p->max_pages;
+    }
+    if (p->seqlens_host) {
+        for (int b = 0; b < p->batch; ++b) {
+            const int32_t L = p->seqlens_host[b];
+            if (L < p->s_q || (int64_t)L > ap.capacity)
+                return fail(ctx, MLA_ERR_INVALID_ARG, "seqlens[%d] = %d outside [s_q = %d, capacity = %lld]", b, L,
+                            p->s_q, (long long)ap.capacity);
+        }
+    }
+    hipLaunchKernelGGL(append_kernel, dim3(p->batch * p->s_q), dim3(64), 0, ctx->stream, ap);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, "append_kernel launch");
+}
+
+int mla_absorb_q(mla_ctx *ctx, const void *q_nope, const void *q_rope, const void *w_uk, void *q_out,
+                 int32_t rows, int32_t heads, int32_t d_nope) {
+    using namespace mla_steps;
+    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->err.clear();
+    if (!q_nope || !q_rope || !w_uk || !q_out)
+        return fail(ctx, MLA_ERR_INVALID_ARG, "q_nope, q_rope, w_uk and q_out must be non-NULL");
+    if (rows < 1 || heads < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "rows and heads must be >= 1");
+    if (d_nope < 32 || d_nope % 32)
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "d_nope must be a positive multiple of 32 (got %d)", d_nope);
+    if (heads > 65535 || (rows + 15) / 16 > 65535 || (int64_t)heads * d_nope > (1 << 20))
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "rows or heads too large");
+    if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_out))
+        return fail(ctx, MLA_ERR_INVALID_ARG, "q_nope, q_rope, w_uk and q_out must be 16-byte aligned");
+    AbsorbParams ap{static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(q_rope),
+                    static_cast<const uint16_t *>(w_uk), static_cast<uint16_t *>(q_out), rows, heads, d_nope};
+    hipLaunchKernelGGL(absorb_kernel, dim3(kLatent / kTileCh, heads, (rows + 15) / 16), dim3(64), 0, ctx->stream,
+                       ap);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, "absorb_kernel launch");
+}
+
+int mla_project_out(mla_ctx *ctx, const float *o, const void *w_uv, float *out, int32_t rows, int32_t heads,
+                    int32_t d_v) {
+    using namespace mla_steps;
+    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->err.clear();
+    if (!o || !w_uv || !out) return fail(ctx, MLA_ERR_INVALID_ARG, "o, w_uv and out must be non-NULL");
+    if (rows < 1 || heads < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "rows and heads must be >= 1");
+    if (d_v < kTileCh || d_v % kTileCh)
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "d_v must be a positive multiple of %d (got %d)", kTileCh, d_v);
+    if (heads > 65535 || (rows + 15) / 16 > 65535 || d_v / kTileCh > 65535)
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "rows, heads or d_v too large");
+    if (!aligned16(o) || !aligned16(w_uv) || !aligned16(out))
+        return fail(ctx, MLA_ERR_INVALID_ARG, "o, w_uv and out must be 16-byte aligned");
+    ProjectParams pp{o, static_cast<const uint16_t *>(w_uv), out, rows, heads, d_v};
+    hipLaunchKernelGGL(project_kernel, dim3(d_v / kTileCh, heads, (rows + 15) / 16), dim3(64), 0, ctx->stream, pp);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, "project_kernel launch");
+}
+
+}  // extern "C"

@@ -207,6 +207,67 @@ int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits,
              int64_t min_chunk, mla_plan_segment *segs, int32_t max_segs,
              int32_t *n_segs, mla_plan_info *info);
 
+/* ------------------------------------------------------------------------
+ * The MLA steps on either side of the attention.  MLA's low-rank joint
+ * compression keeps one latent row per token (gist.science technical
+ * summary, Integration and Implementation); the 576-wide row is read as the
+ * 512-channel compressed KV followed by the 64-channel rotary key, and the
+ * per-head up-projections are absorbed into the query and applied to the
+ * attention output.  The per-head dimensions d_nope (query part without
+ * rotary embedding) and d_v (value head) are arguments: the pages do not fix
+ * them (DeepSeek-V3's are 128 and 128).  All three run on the context's
+ * stream and never allocate.
+ */
+
+/*
+ * Latent-cache append: the s_q new latent rows of each sequence become keys
+ * L_b - s_q .. L_b - 1 of that sequence (token t at key L_b - s_q + t), in
+ * the contiguous or the paged layout of mla_decode.  A byte copy.
+ *
+ *  new_rows     bf16 [B][s_q][576], 16-byte aligned.
+ *  kv_cache     the cache of mla_decode (written), 16-byte aligned.
+ *  block_table, seqlens, p   as for mla_decode; p->num_heads is not used.
+ *               L_b are the lengths including the new tokens.
+ *
+ * Lengths outside [s_q, capacity] (device lengths are not checked on the
+ * host when p->seqlens_host is NULL) are clamped to it; page ids are
+ * clamped into the pool.
+ */
+int mla_append_kv(mla_ctx *ctx, const void *new_rows, void *kv_cache, const int32_t *block_table,
+                  const int32_t *seqlens, const mla_problem *p);
+
+/*
+ * Absorbed query: for every row r (a query token of a sequence) and head h,
+ *   q_out[r][h][c]       = bf16( sum_{d<d_nope} q_nope[r][h][d] * w_uk[h][c][d] ),  c < 512
+ *   q_out[r][h][512 + j] = q_rope[r][h][j],                                            j < 64
+ * i.e. the key up-projection of head h applied to its query, so that q.k
+ * over the latent row equals the score against the up-projected key.
+ * Accumulation in fp32, one rounding to bf16 (to nearest even).
+ *
+ *  q_nope  bf16 [rows][H][d_nope];  q_rope bf16 [rows][H][64]  (rotary
+ *          embedding already applied);  w_uk bf16 [H][512][d_nope]: row c
+ *          of head h holds the weights of latent channel c;  q_out bf16
+ *          [rows][H][576], the query of mla_decode.  All 16-byte aligned.
+ *  rows >= 1; heads >= 1; d_nope a positive multiple of 32.
+ */
+int mla_absorb_q(mla_ctx *ctx, const void *q_nope, const void *q_rope, const void *w_uk, void *q_out,
+                 int32_t rows, int32_t heads, int32_t d_nope);
+
+/*
+ * Output up-projection: for every row r and head h,
+ *   out[r][h][e] = sum_{c<512} o[r][h][c] * w_uv[h][e][c],   e < d_v
+ * applied to the latent attention output o of mla_decode.  fp32 in, fp32
+ * out; o enters the products split into a bf16 high and low part, so it
+ * keeps about 16 significant bits.
+ *
+ *  o      fp32 [rows][H][512];  w_uv bf16 [H][d_v][512] (row e of head h
+ *         holds the weights of value channel e);  out fp32 [rows][H][d_v].
+ *         All 16-byte aligned.
+ *  rows >= 1; heads >= 1; d_v a positive multiple of 64.
+ */
+int mla_project_out(mla_ctx *ctx, const float *o, const void *w_uv, float *out, int32_t rows, int32_t heads,
+                    int32_t d_v);
+
 /* Library version string, e.g. "mla_decode 0.1 gfx950". */
 const char *mla_version(void);
 

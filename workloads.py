@@ -181,3 +181,52 @@ def small(name: str, batch: int, s_q: int, heads: int, seqlens: Sequence[int],
     """A small test shape with explicit per-sequence lengths."""
     w = Workload(name, batch, s_q, heads, int(max(seqlens)), page_size, seed)
     return make_inputs(w, poison=True, seqlens=seqlens)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the MLA steps around the attention (query absorption, output
+# up-projection, cache append).  The per-head widths are not fixed by the
+# pages; DeepSeek-V3's 128 (query without rotary part) and 128 (value head)
+# are the defaults.  Weights are standard normals scaled by 1/sqrt(fan-in),
+# so the absorbed query has unit variance like the attention's query and
+# the projected output the magnitude of the latent output.
+
+D_NOPE = 128
+D_VHEAD = 128
+D_ROPE = D_QK - D_V
+
+
+@dataclasses.dataclass
+class StepInputs:
+    q_nope: np.ndarray    # [rows, H, d_nope] uint16
+    q_rope: np.ndarray    # [rows, H, 64] uint16
+    w_uk: np.ndarray      # [H, 512, d_nope] uint16
+    w_uv: np.ndarray      # [H, d_v, 512] uint16
+    new_rows: np.ndarray  # [B, s_q, 576] uint16: latent rows of the new tokens
+    o: np.ndarray         # [rows, H, 512] float32: stand-in latent attention output
+
+
+def make_step_inputs(seed: int, batch: int, s_q: int, heads: int,
+                     d_nope: int = D_NOPE, d_v: int = D_VHEAD) -> StepInputs:
+    """Seeded step inputs; rows = batch * s_q.  Streams: ``[seed, 3, k]`` for
+    the k-th array, so each is independent of the others' sizes."""
+    rows = batch * s_q
+
+    def normal(k, shape, scale=1.0):
+        return np.random.default_rng([seed, 3, k]).standard_normal(shape, dtype=np.float32) * np.float32(scale)
+
+    return StepInputs(
+        q_nope=f32_to_bf16_bits(normal(0, (rows, heads, d_nope))),
+        q_rope=f32_to_bf16_bits(normal(1, (rows, heads, D_ROPE))),
+        w_uk=f32_to_bf16_bits(normal(2, (heads, D_V, d_nope), 1.0 / math.sqrt(d_nope))),
+        w_uv=f32_to_bf16_bits(normal(3, (heads, d_v, D_V), 1.0 / math.sqrt(D_V))),
+        new_rows=f32_to_bf16_bits(normal(4, (batch, s_q, D_QK))),
+        o=normal(5, (rows, heads, D_V)),
+    )
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda:0"):
+    """Upload uint16 bf16 bit patterns as a torch bfloat16 tensor."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)

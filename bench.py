@@ -17,7 +17,10 @@ step streams it from HBM).  Prints one JSON line.
              the host cores (a reported baseline, not a target)
 
 Other modes: --workload NAME (any of workloads.WORKLOADS), --calibrate-copy
-(a plain 1 GiB device copy, the reference for the HBM byte counters).
+(a plain 1 GiB device copy, the reference for the HBM byte counters),
+--sweep (context length and head count grid), --mla-steps (the absorbed
+query, output projection and cache append around the attention, and a
+whole decode step).
 """
 from __future__ import annotations
 
@@ -159,6 +162,167 @@ def sweep(args) -> int:
     return 0
 
 
+def mla_steps(args) -> int:
+    """The MLA steps around the attention at decode sizes, one JSON line
+    each: absorbed query, output up-projection, latent-cache append, then
+    one whole decode step (absorb, append, attend, project) on the default
+    workload.  The projections read each head's weights once per call; the
+    weights rotate over copies totalling >= 1 GiB per matrix, as the layers
+    of a model would, so every call streams them from HBM.  Algorithmic
+    bytes: every input byte read once plus every output byte written once.
+
+    ``us_per_call`` is GPU time: N calls captured in a HIP graph, replayed,
+    timed with events on the graph's stream (launch gaps inside the graph
+    included, the Python binding's host time excluded).
+    ``us_per_call_eager`` times the same calls made one by one from Python,
+    where the host side of each call can be the longer part."""
+    import torch
+
+    import decode_attention_mla_amd as mla
+    import workloads as wl
+
+    B, s_q, H = (int(x) for x in args.step_shape.split(","))
+    dn, dv = wl.D_NOPE, wl.D_VHEAD
+    rows = B * s_q
+    dev = "cuda:0"
+    si = wl.make_step_inputs(9000, B, s_q, H)
+    ctx = mla.Context()
+    stream = torch.cuda.Stream()
+    gctx = mla.Context(stream=stream)
+
+    def copies_of(t, limit=2048):
+        n = max(1, min(limit, (1 << 30) // (t.numel() * t.element_size())))
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    def settle(fn):
+        s0 = time.perf_counter()
+        while time.perf_counter() - s0 < args.settle_s:
+            for i in range(50):
+                fn(ctx, i)
+            torch.cuda.synchronize()
+        for i in range(args.warmup):
+            fn(ctx, i)
+        torch.cuda.synchronize()
+
+    def eager(fn, k):
+        settle(fn)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(k):
+            fn(ctx, i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k
+
+    def graphed(fn, n, reps):
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            fn(gctx, 0)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(gctx, i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                g.replay()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / (n * reps)
+
+    def report(step, us, us_eager, nbytes, extra=None):
+        line = {"mode": "mla-steps", "step": step, "batch": B, "s_q": s_q, "heads": H,
+                "d_nope": dn, "d_v": dv, "us_per_call": round(us, 3),
+                "us_per_call_eager": round(us_eager, 3),
+                "algorithmic_bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                "frac_of_8TBps": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+        line.update(extra or {})
+        print(json.dumps(line), flush=True)
+
+    k = max(args.steps, 200)
+    qn, qr = wl.bf16_tensor(si.q_nope), wl.bf16_tensor(si.q_rope)
+    w_uk = copies_of(wl.bf16_tensor(si.w_uk))
+    q_out = torch.empty((rows, H, 576), dtype=torch.bfloat16, device=dev)
+
+    def absorb(c, i):
+        mla.mla_absorb_q(c, qn, qr, w_uk[i % len(w_uk)], q_out=q_out)
+
+    us_e = eager(absorb, k)
+    report("absorb_q", graphed(absorb, 256, 4), us_e, H * 512 * dn * 2 + rows * H * (dn + 64 + 576) * 2,
+           {"weight_copies": len(w_uk)})
+    del w_uk
+
+    o = torch.from_numpy(si.o).to(dev)
+    w_uv = copies_of(wl.bf16_tensor(si.w_uv))
+    out = torch.empty((rows, H, dv), dtype=torch.float32, device=dev)
+
+    def project(c, i):
+        mla.mla_project_out(c, o, w_uv[i % len(w_uv)], out=out)
+
+    us_e = eager(project, k)
+    report("project_out", graphed(project, 256, 4), us_e, H * dv * 512 * 2 + rows * H * (512 + dv) * 4,
+           {"weight_copies": len(w_uv)})
+    del w_uv
+
+    # The append and the whole step run on the default workload's cache;
+    # its lengths already count the new token, so the append writes the last
+    # key of each sequence and the attention reads it.  Device lengths only
+    # (as a captured serving loop would pass them).
+    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
+    assert (w.batch, w.s_q) == (B, s_q) and w.page_size == 0, "step shape must match the workload"
+    inp = wl.make_inputs(w)
+    q, kv, bt, lens = wl.to_torch(inp, dev)
+    new_rows = wl.bf16_tensor(si.new_rows)
+
+    def append(c, i):
+        mla.mla_append_kv(c, new_rows, kv, bt, lens)
+
+    us_e = eager(append, k)
+    report("append_kv", graphed(append, 256, 4), us_e, 2 * rows * 576 * 2 + B * 4)
+
+    o_lat = torch.empty((B, s_q, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+    w_uk = copies_of(wl.bf16_tensor(si.w_uk), 64)
+    w_uv = copies_of(wl.bf16_tensor(si.w_uv), 64)
+    qn4, qr4 = qn.view(B, s_q, H, dn), qr.view(B, s_q, H, 64)
+    q_abs = torch.empty((B, s_q, H, 576), dtype=torch.bfloat16, device=dev)
+    out4 = out.view(B, s_q, H, dv)
+    ctx.reserve(s_q, H)
+    gctx.reserve(s_q, H)
+
+    def decode_only(c, i):
+        mla.mla_decode(c, q_abs, kv, bt, lens, inp.scale, out=o_lat, lse=lse)
+
+    def whole(c, i):
+        mla.mla_absorb_q(c, qn4, qr4, w_uk[i % len(w_uk)], q_out=q_abs)
+        mla.mla_append_kv(c, new_rows, kv, bt, lens)
+        decode_only(c, i)
+        mla.mla_project_out(c, o_lat, w_uv[i % len(w_uv)], out=out4)
+
+    ks = max(args.steps, 20)
+    us_dec_e = eager(decode_only, ks)
+    us_all_e = eager(whole, ks)
+    us_dec = graphed(decode_only, 16, 4)
+    us_all = graphed(whole, 16, 4)
+    # KV and weights once; per (row, head): q_nope and q_rope read, the
+    # absorbed query written and read, the latent output written and read,
+    # the projected output written; the appended rows read and written.
+    step_bytes = inp.kv_bytes + H * 512 * (dn + dv) * 2 \
+        + rows * H * (2 * dn + 2 * 64 + 2 * 576 * 2 + 4 * 512 * 2 + 4 * dv) + 2 * rows * 576 * 2
+    report("decode_step", us_all, us_all_e, step_bytes,
+           {"workload": w.name, "attention_only_us": round(us_dec, 3),
+            "attention_only_us_eager": round(us_dec_e, 3),
+            "steps_overhead_us": round(us_all - us_dec, 3)})
+    gctx.close()
+    ctx.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +339,10 @@ def main() -> int:
                     help="GB/s against context length (bs16, bs32) and head count; one line per point")
     ap.add_argument("--sweep-points", default="",
                     help="restrict the sweep to BxHxL points, comma-separated (e.g. 16x16x512)")
+    ap.add_argument("--mla-steps", action="store_true",
+                    help="time the absorbed query, the output projection, the cache append and a "
+                         "whole decode step; one line each")
+    ap.add_argument("--step-shape", default="16,1,16", help="B,s_q,H of --mla-steps")
     ap.add_argument("--splits", type=int, default=0, help="key ranges per launch (0: library default)")
     ap.add_argument("--min-chunk", type=int, default=0, help="smallest key range (0: library default)")
     args = ap.parse_args()
@@ -196,6 +364,8 @@ def main() -> int:
         return 0
     if args.sweep:
         return sweep(args)
+    if args.mla_steps:
+        return mla_steps(args)
 
     name = args.workload or wl.HEADLINE
     w = wl.WORKLOADS[name]

@@ -30,7 +30,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 constexpr int kLatent = MLA_HEAD_DIM_V;                // 512 compressed channels
 constexpr int kRope = MLA_HEAD_DIM_QK - MLA_HEAD_DIM_V;  // 64 rotary channels
 constexpr int kRowBytes = MLA_HEAD_DIM_QK * 2;          // 1152
-constexpr int kTileCh = 64;                             // output channels per wave (4 MFMA tiles)
 
 struct AppendParams {
     const uint16_t *rows;  // [B][s_q][576]
@@ -45,10 +44,16 @@ struct AppendParams {
     int32_t max_pages;
 };
 
-// One wave per new row: 72 chunks of 16 bytes.
+// One wave per new row: 72 chunks of 16 bytes.  The row is loaded before the
+// length (and page id) that places it, so the two memory round trips overlap.
 __global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
     const int row = blockIdx.x;  // b * s_q + t
+    const int lane = threadIdx.x;
     const int b = row / p.s_q, t = row % p.s_q;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(p.rows + (int64_t)row * MLA_HEAD_DIM_QK);
+    constexpr int kChunks = kRowBytes / 16;  // 72
+    const u32x4 v0 = src[lane];
+    const u32x4 v1 = src[64 + (lane < kChunks - 64 ? lane : kChunks - 65)];  // no branch around loads
     int64_t L = p.seqlens[b];
     L = L < p.s_q ? p.s_q : (L > p.capacity ? p.capacity : L);
     const int64_t key = L - p.s_q + t;
@@ -60,20 +65,31 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
     } else {
         dst_row = (int64_t)b * p.kv_capacity + key;
     }
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(p.rows + (int64_t)row * MLA_HEAD_DIM_QK);
     u32x4 *dst = reinterpret_cast<u32x4 *>(p.kv + dst_row * MLA_HEAD_DIM_QK);
-    for (int c = threadIdx.x; c < kRowBytes / 16; c += 64) dst[c] = src[c];
+    dst[lane] = v0;
+    if (lane < kChunks - 64) dst[64 + lane] = v1;
 }
 
-// The B operand of a 16x16x32 MFMA (or the A operand, same layout) for row
-// block `r0`: lane l gets 8 consecutive bf16 of row r0 + l%16 at column
-// 8(l/16) + k0, or zeros past the last row.
+// One MFMA operand (16x16x32, A or B: same layout) from 16 rows of `base`
+// starting at row r0: lane l gets 8 consecutive bf16 of row r0 + l%16 at
+// column k0 + 8(l/16).  Rows at or past `rows` read row rows-1 instead (no
+// branch around the load); `zero_past` then clears them, after the wave has
+// issued all its loads.
 __device__ inline bf16x8 load_rows8(const uint16_t *base, int64_t row_stride, int r0, int rows, int k0,
                                     int lane) {
     const int r = r0 + (lane & 15);
-    if (r >= rows) return bf16x8{};
-    return *reinterpret_cast<const bf16x8 *>(base + (int64_t)r * row_stride + k0 + 8 * (lane >> 4));
+    return *reinterpret_cast<const bf16x8 *>(base + (int64_t)(r < rows ? r : rows - 1) * row_stride + k0 +
+                                             8 * (lane >> 4));
 }
+
+__device__ inline bf16x8 zero_past(bf16x8 v, int r0, int rows, int lane) {
+    return r0 + (lane & 15) < rows ? v : bf16x8{};
+}
+
+// The projections take the 16-row tiles of up to kMaxTiles x 16 rows in one
+// wave, with one load of its weights; the launch picks the fewest tiles that
+// cover the rows (1, 2 or 4).
+constexpr int kMaxTiles = 4;
 
 struct AbsorbParams {
     const uint16_t *q_nope;  // [rows][H][d_nope]
@@ -83,48 +99,90 @@ struct AbsorbParams {
     int32_t rows, heads, d_nope;
 };
 
-// Wave (cg, h, rt): latent channels 64cg .. 64cg+63 of head h for rows
-// 16rt .. 16rt+15.  q_lat^T (channels x rows) = W_UK[h] (channels x d_nope)
-// . q_nope^T (d_nope x rows): A from the weight rows, B from the query rows,
-// both 16 contiguous bytes per lane; D lane l: row l%16, channels
-// 16ct + 4(l/16) .. +3, stored as 4 bf16.  The wave of channel group 0 also
-// copies the rotary part of its rows.
+// One wave per (cg, h, rg): latent channels 16cg .. 16cg+15 of head h for
+// the up to 16 kTiles rows from 16 kTiles rg.
+// q_lat^T (channels x rows) = W_UK[h] (channels x d_nope) . q_nope^T
+// (d_nope x rows): A from the weight rows, B from the query rows, 16
+// contiguous bytes per lane each.  The reduction dimension goes in chunks of
+// 128 whose loads (weights once, queries per tile) are all issued before
+// the first MFMA, so the wave waits for memory once per chunk (once, for
+// d_nope <= 128).  D lane l: row l%16 of the tile, channels 4(l/16) .. +3,
+// stored as 4 bf16.  The waves of channel group 0 also copy the rotary
+// part of their rows.
+constexpr int kAbsorbChunk = 128;
+
+template <int kTiles>
 __global__ __launch_bounds__(64) void absorb_kernel(AbsorbParams p) {
     const int lane = threadIdx.x;
-    const int cg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16;
+    const int cg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16 * kTiles;
+    const int ch0 = cg * 16;
     const int64_t q_stride = (int64_t)p.heads * p.d_nope;  // between rows
     const uint16_t *qn = p.q_nope + (int64_t)h * p.d_nope;
-    const uint16_t *w = p.w_uk + ((int64_t)h * kLatent + cg * kTileCh) * p.d_nope;
-    f32x4 acc[4] = {};
-    for (int k0 = 0; k0 < p.d_nope; k0 += 32) {
-        const bf16x8 bq = load_rows8(qn, q_stride, r0, p.rows, k0, lane);
-        bf16x8 aw[4];
+    const uint16_t *w = p.w_uk + ((int64_t)h * kLatent + ch0) * p.d_nope;
+    constexpr int kK = kAbsorbChunk / 32;
+    f32x4 acc[kTiles] = {};
+    for (int c0 = 0; c0 < p.d_nope; c0 += kAbsorbChunk) {
+        bf16x8 aw[kK], bq[kTiles][kK];
+        // Reduction steps past d_nope load the last step again (no branch
+        // around the loads) and are zeroed; so are rows past the last.
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) aw[ct] = load_rows8(w + ct * 16 * p.d_nope, p.d_nope, 0, 16, k0, lane);
+        for (int s = 0; s < kK; ++s) {
+            const int k0 = c0 + 32 * s;
+            aw[s] = load_rows8(w, p.d_nope, 0, 16, k0 < p.d_nope ? k0 : p.d_nope - 32, lane);
+        }
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ct], bq, acc[ct], 0, 0, 0);
+        for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+            for (int s = 0; s < kK; ++s) {
+                const int k0 = c0 + 32 * s;
+                bq[t][s] = load_rows8(qn, q_stride, r0 + 16 * t, p.rows, k0 < p.d_nope ? k0 : p.d_nope - 32, lane);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the chunk in flight before any is used
+#pragma unroll
+        for (int s = 0; s < kK; ++s) aw[s] = c0 + 32 * s < p.d_nope ? aw[s] : bf16x8{};
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+            for (int s = 0; s < kK; ++s) bq[t][s] = zero_past(bq[t][s], r0 + 16 * t, p.rows, lane);
+        }
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+            for (int s = 0; s < kK; ++s) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[s], bq[t][s], acc[t], 0, 0, 0);
+        }
     }
-    const int r = r0 + (lane & 15);
-    if (r < p.rows) {
-        uint16_t *out = p.q_out + ((int64_t)r * p.heads + h) * MLA_HEAD_DIM_QK + cg * kTileCh + 4 * (lane >> 4);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+    for (int t = 0; t < kTiles; ++t) {
+        const int r = r0 + 16 * t + (lane & 15);
+        if (r < p.rows) {
             bf16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(acc[ct][i]);  // to nearest even
-            *reinterpret_cast<bf16x4 *>(out + 16 * ct) = v;
+            for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(acc[t][i]);  // to nearest even
+            *reinterpret_cast<bf16x4 *>(p.q_out + ((int64_t)r * p.heads + h) * MLA_HEAD_DIM_QK + ch0 + 4 * (lane >> 4)) = v;
         }
     }
     if (cg == 0) {
-        // Rotary part: 16 rows x 128 B, lane l -> row l/4, 32 bytes.
-        const int rr = r0 + (lane >> 2);
-        if (rr < p.rows) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(p.q_rope + ((int64_t)rr * p.heads + h) * kRope) +
+        // Rotary part: 128 B per row, lane l -> row l/4 of each 16, 32 bytes.
+        u32x4 v[kTiles][2];
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+            const int rr = r0 + 16 * t + (lane >> 2);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                                   p.q_rope + ((int64_t)(rr < p.rows ? rr : p.rows - 1) * p.heads + h) * kRope) +
                                2 * (lane & 3);
-            u32x4 *dst = reinterpret_cast<u32x4 *>(p.q_out + ((int64_t)rr * p.heads + h) * MLA_HEAD_DIM_QK + kLatent) +
-                         2 * (lane & 3);
-            dst[0] = src[0];
-            dst[1] = src[1];
+            v[t][0] = src[0];
+            v[t][1] = src[1];
+        }
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+            const int rr = r0 + 16 * t + (lane >> 2);
+            if (rr < p.rows) {
+                u32x4 *dst = reinterpret_cast<u32x4 *>(p.q_out + ((int64_t)rr * p.heads + h) * MLA_HEAD_DIM_QK + kLatent) +
+                             2 * (lane & 3);
+                dst[0] = v[t][0];
+                dst[1] = v[t][1];
+            }
         }
     }
 }
@@ -136,49 +194,84 @@ struct ProjectParams {
     int32_t rows, heads, d_v;
 };
 
-// Wave (eg, h, rt): value channels 64eg .. 64eg+63 of head h for rows
-// 16rt .. 16rt+15.  out^T (d_v x rows) = W_UV[h] (d_v x 512) . o^T
-// (512 x rows): A from the weight rows, B from the output rows split into
-// bf16 hi + lo (two MFMAs per k step); D lane l: row l%16, channels
-// 16ct + 4(l/16) .. +3, stored as 16 bytes.
-__global__ __launch_bounds__(64) void project_kernel(ProjectParams p) {
-    const int lane = threadIdx.x;
-    const int eg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16;
-    const int r = r0 + (lane & 15);
-    const bool live = r < p.rows;
-    const float *orow = p.o + ((int64_t)r * p.heads + h) * kLatent + 8 * (lane >> 4);
-    const uint16_t *w = p.w_uv + ((int64_t)h * p.d_v + eg * kTileCh) * kLatent;
-    f32x4 acc[4] = {};
-    for (int k0 = 0; k0 < kLatent; k0 += 32) {
-        f32x4 x0 = {}, x1 = {};
-        if (live) {
-            x0 = *reinterpret_cast<const f32x4 *>(orow + k0);
-            x1 = *reinterpret_cast<const f32x4 *>(orow + k0 + 4);
+// Workgroup (eg, h, rg) of eight waves: value channels 16eg .. 16eg+15 of
+// head h for the up to 16 kTiles rows from 16 kTiles rg;
+// wave w takes latent channels 64w .. 64w+63 of the reduction.  out^T
+// (d_v x rows) = W_UV[h] (d_v x 512) . o^T (512 x rows): A from the weight
+// rows (loaded once for all tiles), B from the output rows split into bf16
+// hi + lo (two MFMAs per 32 channels).  All of a wave's loads are issued
+// before its first MFMA.  The eight partial tiles are summed through LDS in
+// wave order (the same order on every run); D lane l: row l%16 of the tile,
+// channels 4(l/16) .. +3, stored as 16 bytes.
+constexpr int kProjectWaves = 8;
+constexpr int kProjectSlice = kLatent / kProjectWaves;  // 64
+
+template <int kTiles>
+__global__ __launch_bounds__(64 * kProjectWaves) void project_kernel(ProjectParams p) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int eg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16 * kTiles;
+    const int k = wv * kProjectSlice + 8 * (lane >> 4);
+    const uint16_t *w = p.w_uv + ((int64_t)h * p.d_v + eg * 16 + (lane & 15)) * kLatent + k;
+    constexpr int kSteps = kProjectSlice / 32;
+    bf16x8 aw[kSteps];
+    f32x4 x[kTiles][2 * kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) aw[s] = *reinterpret_cast<const bf16x8 *>(w + 32 * s);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        // Lanes past the last row read the last row (no branch around the
+        // loads) and zero it.
+        const int r = r0 + 16 * t + (lane & 15);
+        const float *orow = p.o + ((int64_t)(r < p.rows ? r : p.rows - 1) * p.heads + h) * kLatent + k;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            x[t][2 * s] = *reinterpret_cast<const f32x4 *>(orow + 32 * s);
+            x[t][2 * s + 1] = *reinterpret_cast<const f32x4 *>(orow + 32 * s + 4);
         }
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float x = j < 4 ? x0[j] : x1[j - 4];
-            const __bf16 hb = static_cast<__bf16>(x);
-            hi[j] = hb;
-            lo[j] = static_cast<__bf16>(x - static_cast<float>(hb));
-        }
-        bf16x8 aw[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) aw[ct] = load_rows8(w + ct * 16 * kLatent, kLatent, 0, 16, k0, lane);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ct], hi, acc[ct], 0, 0, 0);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ct], lo, acc[ct], 0, 0, 0);
     }
-    if (live) {
-        float *out = p.out + ((int64_t)r * p.heads + h) * p.d_v + eg * kTileCh + 4 * (lane >> 4);
+    __builtin_amdgcn_sched_barrier(0);  // every load in flight before any is used
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) *reinterpret_cast<f32x4 *>(out + 16 * ct) = acc[ct];
+    for (int t = 0; t < kTiles; ++t) {
+        const bool live = r0 + 16 * t + (lane & 15) < p.rows;
+#pragma unroll
+        for (int i = 0; i < 2 * kSteps; ++i) x[t][i] = live ? x[t][i] : f32x4{};
+    }
+    __shared__ f32x4 part[kProjectWaves][kTiles][64];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        f32x4 acc = {};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xv = x[t][2 * s + j / 4][j % 4];
+                const __bf16 hb = static_cast<__bf16>(xv);
+                hi[j] = hb;
+                lo[j] = static_cast<__bf16>(xv - static_cast<float>(hb));
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[s], hi, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[s], lo, acc, 0, 0, 0);
+        }
+        part[wv][t][lane] = acc;
+    }
+    __syncthreads();
+    // Thread i sums tile i/64, lane i%64 over the eight waves.
+    if (threadIdx.x < 64 * kTiles) {
+        const int t = threadIdx.x >> 6;
+        const int r = r0 + 16 * t + (lane & 15);
+        if (r < p.rows) {
+            f32x4 sum = part[0][t][lane];
+#pragma unroll
+            for (int i = 1; i < kProjectWaves; ++i) sum += part[i][t][lane];
+            *reinterpret_cast<f32x4 *>(p.out + ((int64_t)r * p.heads + h) * p.d_v + eg * 16 + 4 * (lane >> 4)) = sum;
+        }
     }
 }
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+int tiles_for(int rows) { return rows <= 16 ? 1 : rows <= 32 ? 2 : kMaxTiles; }
 
 }  // namespace mla_steps
 
@@ -258,8 +351,14 @@ int mla_absorb_q(mla_ctx *ctx, const void *q_nope, const void *q_rope, const voi
         return fail(ctx, MLA_ERR_INVALID_ARG, "q_nope, q_rope, w_uk and q_out must be 16-byte aligned");
     AbsorbParams ap{static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(q_rope),
                     static_cast<const uint16_t *>(w_uk), static_cast<uint16_t *>(q_out), rows, heads, d_nope};
-    hipLaunchKernelGGL(absorb_kernel, dim3(kLatent / kTileCh, heads, (rows + 15) / 16), dim3(64), 0, ctx->stream,
-                       ap);
+    const int tiles = tiles_for(rows);
+    const dim3 grid(kLatent / 16, heads, (rows + 16 * tiles - 1) / (16 * tiles));
+    if (tiles == 1)
+        hipLaunchKernelGGL(absorb_kernel<1>, grid, dim3(64), 0, ctx->stream, ap);
+    else if (tiles == 2)
+        hipLaunchKernelGGL(absorb_kernel<2>, grid, dim3(64), 0, ctx->stream, ap);
+    else
+        hipLaunchKernelGGL(absorb_kernel<kMaxTiles>, grid, dim3(64), 0, ctx->stream, ap);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, "absorb_kernel launch");
 }
@@ -271,14 +370,21 @@ int mla_project_out(mla_ctx *ctx, const float *o, const void *w_uv, float *out, 
     ctx->err.clear();
     if (!o || !w_uv || !out) return fail(ctx, MLA_ERR_INVALID_ARG, "o, w_uv and out must be non-NULL");
     if (rows < 1 || heads < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "rows and heads must be >= 1");
-    if (d_v < kTileCh || d_v % kTileCh)
-        return fail(ctx, MLA_ERR_UNSUPPORTED, "d_v must be a positive multiple of %d (got %d)", kTileCh, d_v);
-    if (heads > 65535 || (rows + 15) / 16 > 65535 || d_v / kTileCh > 65535)
+    if (d_v < 16 || d_v % 16)
+        return fail(ctx, MLA_ERR_UNSUPPORTED, "d_v must be a positive multiple of 16 (got %d)", d_v);
+    if (heads > 65535 || (rows + 15) / 16 > 65535 || d_v / 16 > 65535)
         return fail(ctx, MLA_ERR_UNSUPPORTED, "rows, heads or d_v too large");
     if (!aligned16(o) || !aligned16(w_uv) || !aligned16(out))
         return fail(ctx, MLA_ERR_INVALID_ARG, "o, w_uv and out must be 16-byte aligned");
     ProjectParams pp{o, static_cast<const uint16_t *>(w_uv), out, rows, heads, d_v};
-    hipLaunchKernelGGL(project_kernel, dim3(d_v / kTileCh, heads, (rows + 15) / 16), dim3(64), 0, ctx->stream, pp);
+    const int tiles = tiles_for(rows);
+    const dim3 grid(d_v / 16, heads, (rows + 16 * tiles - 1) / (16 * tiles));
+    if (tiles == 1)
+        hipLaunchKernelGGL(project_kernel<1>, grid, dim3(64 * kProjectWaves), 0, ctx->stream, pp);
+    else if (tiles == 2)
+        hipLaunchKernelGGL(project_kernel<2>, grid, dim3(64 * kProjectWaves), 0, ctx->stream, pp);
+    else
+        hipLaunchKernelGGL(project_kernel<kMaxTiles>, grid, dim3(64 * kProjectWaves), 0, ctx->stream, pp);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, "project_kernel launch");
 }

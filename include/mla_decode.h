@@ -263,7 +263,7 @@ int mla_absorb_q(mla_ctx *ctx, const void *q_nope, const void *q_rope, const voi
  *  o      fp32 [rows][H][512];  w_uv bf16 [H][d_v][512] (row e of head h
  *         holds the weights of value channel e);  out fp32 [rows][H][d_v].
  *         All 16-byte aligned.
- *  rows >= 1; heads >= 1; d_v a positive multiple of 64.
+ *  rows >= 1; heads >= 1; d_v a positive multiple of 16.
  */
 int mla_project_out(mla_ctx *ctx, const float *o, const void *w_uv, float *out, int32_t rows, int32_t heads,
                     int32_t d_v);

@@ -91,6 +91,8 @@ ABSORB = [
     (33, 5, 64),
     (64, 128, 128),
     (2, 16, 512),
+    (100, 2, 96),      # two 64-row groups, the second ragged
+    (32, 4, 160),
 ]
 
 
@@ -137,6 +139,10 @@ PROJECT = [
     (33, 5, 192),
     (64, 128, 128),
     (2, 16, 512),
+    (5, 3, 16),
+    (40, 2, 48),
+    (100, 4, 32),
+    (32, 2, 128),
 ]
 
 

@@ -225,8 +225,12 @@ def mla_steps(args) -> int:
                 fn(gctx, i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
-            for _ in range(2):
+            s0 = time.perf_counter()  # replays until the clocks settle, as for eager calls
+            while True:
                 g.replay()
+                stream.synchronize()
+                if time.perf_counter() - s0 >= args.settle_s:
+                    break
             e0.record()
             for _ in range(reps):
                 g.replay()

@@ -352,7 +352,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X "
+        print("bench.py measures one GPU: the library runs on a single MI355X "
               "(no collectives); use --gpus 1.", file=sys.stderr)
         return 2
 

@@ -162,3 +162,16 @@ def test_plan_random_fuzz():
         B = int(rng.integers(1, 80))
         lens = rng.integers(1, 5000, size=B)
         check_plan(lens, int(rng.integers(1, 300)), int(rng.choice([64, 128, 256, 1024])))
+
+
+def test_smoke_case_passes_host_validation():
+    """The smoke check's inputs satisfy the library's own argument checks
+    (s_q <= L_b <= capacity, page geometry), so smoke() cannot fail on them."""
+    import __graft_entry__ as entry
+
+    inp = entry.smoke_inputs()
+    B, s_q, H = inp.q.shape[:3]
+    rc, msg = validate(batch=B, s_q=s_q, num_heads=H, page_size=inp.kv.shape[1], kv_capacity=0,
+                       num_pages=inp.kv.shape[0], max_pages=inp.block_table.shape[1], bt=A,
+                       seqlens_host=inp.seqlens)
+    assert rc == mla.MLA_OK, msg

@@ -59,6 +59,9 @@ SMALL = [
     (1, 4, 32, [129], 64),
     (4, 2, 48, [31, 32, 33, 500], 0),
     (2, 5, 16, [7, 150], 16),           # row blocks 4 + 1: two kernels
+    (2, 1, 48, [300, 70], 16),          # three row blocks: one idle wave
+    (1, 1, 128, [777], 64),             # eight row blocks: two groups of four
+    (1, 2, 64, [1000], 0),              # eight row blocks over two tokens
 ]
 
 

@@ -1414,9 +1414,18 @@ struct LaunchTimer {
     }
 };
 
-int splits_for(const mla_ctx *ctx, int n_rbg) {
+// Row-block groups per launch: groups of four (and a last group of three)
+// go to one launch, a last group of one or two to a second launch after it.
+// The key ranges are sized so that the larger launch fills the GPU once.
+int groups_per_launch(int n_rb) {
+    const int rem = n_rb % mla::kWaves;
+    const int full = n_rb / mla::kWaves + (rem == 3 ? 1 : 0);
+    return std::max(full, (rem == 1 || rem == 2) ? 1 : 0);
+}
+
+int splits_for(const mla_ctx *ctx, int n_rb) {
     if (ctx->opt_splits > 0) return (int)ctx->opt_splits;
-    return std::max(1, ctx->cu_count / n_rbg);
+    return std::max(1, ctx->cu_count / groups_per_launch(n_rb));
 }
 
 size_t workspace_bytes(int splits, int n_rb) {
@@ -1452,8 +1461,7 @@ int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads) {
     if (s_q < 1 || num_heads < 16 || num_heads % 16)
         return fail(ctx, MLA_ERR_INVALID_ARG, "bad s_q / num_heads");
     const int n_rb = s_q * num_heads / 16;
-    const int n_rbg = (n_rb + mla::kWaves - 1) / mla::kWaves;
-    return ensure_workspace(ctx, workspace_bytes(splits_for(ctx, n_rbg), n_rb));
+    return ensure_workspace(ctx, workspace_bytes(splits_for(ctx, n_rb), n_rb));
 }
 
 int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t *block_table,
@@ -1465,8 +1473,7 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t 
     if (rc != MLA_OK) return rc;
 
     const int n_rb = p->s_q * p->num_heads / 16;
-    const int n_rbg = (n_rb + kWaves - 1) / kWaves;
-    const int splits = splits_for(ctx, n_rbg);
+    const int splits = splits_for(ctx, n_rb);
     rc = ensure_workspace(ctx, workspace_bytes(splits, n_rb));
     if (rc != MLA_OK) return rc;
 

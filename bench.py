@@ -339,6 +339,9 @@ def main() -> int:
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="untimed steps for this long before the warmup steps (clock ramp)")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--warm", action="store_true",
+                    help="no rotation over cache copies: a cache that fits the 256 MB last-level cache "
+                         "stays there between steps (the default streams every step from HBM)")
     ap.add_argument("--sweep", action="store_true",
                     help="GB/s against context length (bs16, bs32) and head count; one line per point")
     ap.add_argument("--sweep-points", default="",
@@ -381,7 +384,7 @@ def main() -> int:
     # the cache to stream from HBM on every step.
     copies = [kv]
     dev_bytes = kv.numel() * 2
-    while dev_bytes * len(copies) < (1 << 30) and len(copies) < 16:
+    while not args.warm and dev_bytes * len(copies) < (1 << 30) and len(copies) < 16:
         copies.append(kv.clone())
     out = torch.empty((w.batch, w.s_q, w.heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.batch, w.s_q, w.heads), dtype=torch.float32, device="cuda")
@@ -450,7 +453,7 @@ def main() -> int:
         "config": {"workload": name, "batch": w.batch, "s_q": w.s_q, "heads": w.heads,
                    "kv_len": w.seqlen if isinstance(w.seqlen, int) else list(w.seqlen),
                    "layout": "paged%d" % w.page_size if w.page_size else "contiguous",
-                   "kv_bytes": kv_bytes, "cache_copies_rotated": len(copies),
+                   "kv_bytes": kv_bytes, "cache_copies_rotated": len(copies), "warm": bool(args.warm),
                    "splits": args.splits or "default", "min_chunk": args.min_chunk or "default"},
         "roofline": {
             "bound": "hbm",

@@ -42,10 +42,18 @@ KERNEL_SOURCES = ("decode_attention_mla_amd/csrc/mla_kernels.hip", "decode_atten
 
 
 def kernel_source_hash() -> str:
+    """sha256 of the split kernel's sources with comments and blank space
+    removed: a change to the code invalidates stored counters, a change to
+    a comment does not."""
+    import re
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -106,7 +106,10 @@ int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads);
 /*
  * Tuning knobs (they change speed, never results beyond rounding):
  *  MLA_OPT_NUM_SPLITS  number of key-range workgroups per row-block group
- *                      (default: the device's CU count); 0 restores it.
+ *                      (default: the device's CU count divided by the
+ *                      row-block groups that one launch runs side by side;
+ *                      groups of four row blocks share a launch, a last
+ *                      group of one or two runs in its own); 0 restores it.
  *  MLA_OPT_MIN_CHUNK   smallest key range given to one workgroup (default
  *                      64, rounded up to MLA_KEY_BLOCK); 0 restores it.
  *  MLA_OPT_KERNEL_TIMING  1: bracket every kernel launch with HIP events on

@@ -99,36 +99,40 @@ struct AbsorbParams {
     int32_t rows, heads, d_nope;
 };
 
-// One wave per (cg, h, rg): latent channels 16cg .. 16cg+15 of head h for
-// the up to 16 kTiles rows from 16 kTiles rg.
+// One wave per (cg, h, rg): latent channels 16 kCh cg .. (kCh tiles of 16)
+// of head h for the up to 16 kTiles rows from 16 kTiles rg.
 // q_lat^T (channels x rows) = W_UK[h] (channels x d_nope) . q_nope^T
 // (d_nope x rows): A from the weight rows, B from the query rows, 16
 // contiguous bytes per lane each.  The reduction dimension goes in chunks of
 // 128 whose loads (weights once, queries per tile) are all issued before
 // the first MFMA, so the wave waits for memory once per chunk (once, for
-// d_nope <= 128).  D lane l: row l%16 of the tile, channels 4(l/16) .. +3,
-// stored as 4 bf16.  The waves of channel group 0 also copy the rotary
-// part of their rows.
+// d_nope <= 128).  More channel tiles per wave read the query rows fewer
+// times over.  D lane l: row l%16 of the tile, channels 4(l/16) .. +3 of
+// the channel tile, stored as 4 bf16.  The waves of channel group 0 also
+// copy the rotary part of their rows.
 constexpr int kAbsorbChunk = 128;
 
-template <int kTiles>
+template <int kTiles, int kCh>
 __global__ __launch_bounds__(64) void absorb_kernel(AbsorbParams p) {
     const int lane = threadIdx.x;
     const int cg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16 * kTiles;
-    const int ch0 = cg * 16;
+    const int ch0 = cg * 16 * kCh;
     const int64_t q_stride = (int64_t)p.heads * p.d_nope;  // between rows
     const uint16_t *qn = p.q_nope + (int64_t)h * p.d_nope;
     const uint16_t *w = p.w_uk + ((int64_t)h * kLatent + ch0) * p.d_nope;
     constexpr int kK = kAbsorbChunk / 32;
-    f32x4 acc[kTiles] = {};
+    f32x4 acc[kCh][kTiles] = {};
     for (int c0 = 0; c0 < p.d_nope; c0 += kAbsorbChunk) {
-        bf16x8 aw[kK], bq[kTiles][kK];
+        bf16x8 aw[kCh][kK], bq[kTiles][kK];
         // Reduction steps past d_nope load the last step again (no branch
         // around the loads) and are zeroed; so are rows past the last.
 #pragma unroll
-        for (int s = 0; s < kK; ++s) {
-            const int k0 = c0 + 32 * s;
-            aw[s] = load_rows8(w, p.d_nope, 0, 16, k0 < p.d_nope ? k0 : p.d_nope - 32, lane);
+        for (int c = 0; c < kCh; ++c) {
+#pragma unroll
+            for (int s = 0; s < kK; ++s) {
+                const int k0 = c0 + 32 * s;
+                aw[c][s] = load_rows8(w + 16 * c * p.d_nope, p.d_nope, 0, 16, k0 < p.d_nope ? k0 : p.d_nope - 32, lane);
+            }
         }
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
@@ -140,26 +144,37 @@ __global__ __launch_bounds__(64) void absorb_kernel(AbsorbParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);  // every load of the chunk in flight before any is used
 #pragma unroll
-        for (int s = 0; s < kK; ++s) aw[s] = c0 + 32 * s < p.d_nope ? aw[s] : bf16x8{};
+        for (int c = 0; c < kCh; ++c) {
+#pragma unroll
+            for (int s = 0; s < kK; ++s) aw[c][s] = c0 + 32 * s < p.d_nope ? aw[c][s] : bf16x8{};
+        }
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
             for (int s = 0; s < kK; ++s) bq[t][s] = zero_past(bq[t][s], r0 + 16 * t, p.rows, lane);
         }
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
+        for (int c = 0; c < kCh; ++c) {
 #pragma unroll
-            for (int s = 0; s < kK; ++s) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[s], bq[t][s], acc[t], 0, 0, 0);
+            for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+                for (int s = 0; s < kK; ++s)
+                    acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[c][s], bq[t][s], acc[c][t], 0, 0, 0);
+            }
         }
     }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         const int r = r0 + 16 * t + (lane & 15);
         if (r < p.rows) {
-            bf16x4 v;
+            uint16_t *dst = p.q_out + ((int64_t)r * p.heads + h) * MLA_HEAD_DIM_QK + ch0 + 4 * (lane >> 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(acc[t][i]);  // to nearest even
-            *reinterpret_cast<bf16x4 *>(p.q_out + ((int64_t)r * p.heads + h) * MLA_HEAD_DIM_QK + ch0 + 4 * (lane >> 4)) = v;
+            for (int c = 0; c < kCh; ++c) {
+                bf16x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(acc[c][t][i]);  // to nearest even
+                *reinterpret_cast<bf16x4 *>(dst + 16 * c) = v;
+            }
         }
     }
     if (cg == 0) {
@@ -351,14 +366,19 @@ int mla_absorb_q(mla_ctx *ctx, const void *q_nope, const void *q_rope, const voi
         return fail(ctx, MLA_ERR_INVALID_ARG, "q_nope, q_rope, w_uk and q_out must be 16-byte aligned");
     AbsorbParams ap{static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(q_rope),
                     static_cast<const uint16_t *>(w_uk), static_cast<uint16_t *>(q_out), rows, heads, d_nope};
+    // Few rows: one channel tile per wave, many waves.  More rows: four
+    // channel tiles and four row tiles per wave, so the query rows are read
+    // by 8 waves per head instead of 32.
     const int tiles = tiles_for(rows);
-    const dim3 grid(kLatent / 16, heads, (rows + 16 * tiles - 1) / (16 * tiles));
     if (tiles == 1)
-        hipLaunchKernelGGL(absorb_kernel<1>, grid, dim3(64), 0, ctx->stream, ap);
+        hipLaunchKernelGGL((absorb_kernel<1, 1>), dim3(kLatent / 16, heads, (rows + 15) / 16), dim3(64), 0,
+                           ctx->stream, ap);
     else if (tiles == 2)
-        hipLaunchKernelGGL(absorb_kernel<2>, grid, dim3(64), 0, ctx->stream, ap);
+        hipLaunchKernelGGL((absorb_kernel<2, 1>), dim3(kLatent / 16, heads, (rows + 31) / 32), dim3(64), 0,
+                           ctx->stream, ap);
     else
-        hipLaunchKernelGGL(absorb_kernel<kMaxTiles>, grid, dim3(64), 0, ctx->stream, ap);
+        hipLaunchKernelGGL((absorb_kernel<kMaxTiles, 4>), dim3(kLatent / 64, heads, (rows + 63) / 64), dim3(64), 0,
+                           ctx->stream, ap);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, "absorb_kernel launch");
 }

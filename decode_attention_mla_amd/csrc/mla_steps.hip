@@ -11,9 +11,10 @@
 //   * project: out[h] = W_UV[h] o[h]  (o: the 512-wide latent output).
 //
 // At decode sizes (a few to a few hundred query rows) the projections read
-// each weight once and do 2 x rows flops per weight: they are bound by the
-// weights' HBM bytes up to rows ~ 150, so the kernels below aim at plain
-// coalesced streaming with MFMA doing the arithmetic, not at data reuse.
+// each weight once and do 2 x rows flops per weight: below ~150 rows the
+// weights' HBM bytes bound them, and at a few rows the latency of one
+// memory round trip does.  So the kernels below issue every load of a wave
+// at once and let MFMA do the arithmetic; they do not aim at data reuse.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

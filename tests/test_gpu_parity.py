@@ -238,3 +238,17 @@ def test_workload_full_size(ctx, name, rows):
     law = np.log(vis)[:, :, None] + a2.sum(-1) / 2
     tol = 8 * np.sqrt((np.exp(a2.sum(-1)) - 1) / vis[:, :, None])
     assert np.all(np.abs(l - law) <= tol)
+
+
+def test_long_single_sequence(ctx):
+    """One sequence of 2,000,003 keys (2.3 GB of cache): key byte offsets
+    past 2^31, 256 parts of one sequence merged in 16 batches, a ragged
+    last block; every row against the oracle."""
+    import torch
+
+    announce("long single sequence L=2000003")
+    inp = wl.small("long", 1, 1, 16, [2_000_003], page_size=0, seed=77)
+    o, l = run_gpu(ctx, inp)
+    torch.cuda.empty_cache()
+    ro, rl = oracle_of(inp)
+    compare(o, l, ro, rl, "long single sequence")

@@ -62,6 +62,9 @@ SMALL = [
     (2, 1, 48, [300, 70], 16),          # three row blocks: one idle wave
     (1, 1, 128, [777], 64),             # eight row blocks: two groups of four
     (1, 2, 64, [1000], 0),              # eight row blocks over two tokens
+    (1, 8, 16, [1000], 16),             # eight causal tokens
+    (1, 1, 144, [600], 0),              # nine row blocks: two groups, then one
+    (2, 3, 32, [50, 700], 64),          # six row blocks: a group, then two
 ]
 
 

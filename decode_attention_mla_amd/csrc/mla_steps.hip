@@ -210,17 +210,18 @@ struct ProjectParams {
     int32_t rows, heads, d_v;
 };
 
-// Workgroup (eg, h, rg) of eight waves: value channels 16eg .. 16eg+15 of
-// head h for the up to 16 kTiles rows from 16 kTiles rg;
-// wave w takes latent channels 64w .. 64w+63 of the reduction.  out^T
-// (d_v x rows) = W_UV[h] (d_v x 512) . o^T (512 x rows): A from the weight
-// rows (loaded once for all tiles), B from the output rows split into bf16
-// hi + lo (two MFMAs per 32 channels).  All of a wave's loads are issued
-// before its first MFMA.  The eight partial tiles are summed through LDS in
-// wave order (the same order on every run); D lane l: row l%16 of the tile,
-// channels 4(l/16) .. +3, stored as 16 bytes.
-constexpr int kProjectWaves = 8;
-constexpr int kProjectSlice = kLatent / kProjectWaves;  // 64
+// Workgroup (eg, h, rg) of four waves: value channels 16eg .. 16eg+15 of
+// head h for the up to 16 kTiles rows from 16 kTiles rg; wave w takes
+// latent channels 128w .. 128w+127 of the reduction.  out^T (d_v x rows) =
+// W_UV[h] (d_v x 512) . o^T (512 x rows): A from the weight rows (loaded once
+// for all tiles), B from the output rows split into bf16 hi + lo (two MFMAs
+// per 32 channels).  All of a wave's loads are issued before its first
+// MFMA.  The four partial tiles are summed through LDS in wave order (the
+// same order on every run); D lane l: row l%16 of the tile, channels
+// 4(l/16) .. +3, stored as 16 bytes.  (Eight or sixteen waves per workgroup
+// measured 8% and 6% slower at 128 rows, and no faster at 16.)
+constexpr int kProjectWaves = 4;
+constexpr int kProjectSlice = kLatent / kProjectWaves;  // 128
 
 template <int kTiles>
 __global__ __launch_bounds__(64 * kProjectWaves) void project_kernel(ProjectParams p) {
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(64 * kProjectWaves) void project_kernel(ProjectPara
         part[wv][t][lane] = acc;
     }
     __syncthreads();
-    // Thread i sums tile i/64, lane i%64 over the eight waves.
+    // Thread i sums tile i/64, lane i%64 over the waves.
     if (threadIdx.x < 64 * kTiles) {
         const int t = threadIdx.x >> 6;
         const int r = r0 + 16 * t + (lane & 15);

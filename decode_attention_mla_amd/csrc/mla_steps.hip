@@ -116,7 +116,7 @@ constexpr int kAbsorbChunk = 128;
 template <int kTiles, int kCh>
 __global__ __launch_bounds__(64) void absorb_kernel(AbsorbParams p) {
     const int lane = threadIdx.x;
-    const int cg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16 * kTiles;
+    const int h = blockIdx.x, cg = blockIdx.y, r0 = blockIdx.z * 16 * kTiles;
     const int ch0 = cg * 16 * kCh;
     const int64_t q_stride = (int64_t)p.heads * p.d_nope;  // between rows
     const uint16_t *qn = p.q_nope + (int64_t)h * p.d_nope;
@@ -226,7 +226,7 @@ constexpr int kProjectSlice = kLatent / kProjectWaves;  // 128
 template <int kTiles>
 __global__ __launch_bounds__(64 * kProjectWaves) void project_kernel(ProjectParams p) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int eg = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * 16 * kTiles;
+    const int h = blockIdx.x, eg = blockIdx.y, r0 = blockIdx.z * 16 * kTiles;
     const int k = wv * kProjectSlice + 8 * (lane >> 4);
     const uint16_t *w = p.w_uv + ((int64_t)h * p.d_v + eg * 16 + (lane & 15)) * kLatent + k;
     constexpr int kSteps = kProjectSlice / 32;
@@ -289,6 +289,14 @@ __global__ __launch_bounds__(64 * kProjectWaves) void project_kernel(ProjectPara
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 int tiles_for(int rows) { return rows <= 16 ? 1 : rows <= 32 ? 2 : kMaxTiles; }
+
+// Both projections launch with the head in blockIdx.x.  Workgroups go to
+// the eight XCDs (each with its own L2) in turn by linear id, so with a head
+// count that is a multiple of 8 every workgroup of head h runs on XCD h % 8,
+// and the head's query or latent-output rows are fetched into one L2 only.
+// Measured HBM fetches are then 1.01-1.03x the algorithmic bytes; with the
+// channel group first every XCD fetched every head's rows (projection: 2.4x
+// at 16 rows, 5.7x at 128).
 
 }  // namespace mla_steps
 
@@ -373,13 +381,13 @@ int mla_absorb_q(mla_ctx *ctx, const void *q_nope, const void *q_rope, const voi
     // by 8 waves per head instead of 32.
     const int tiles = tiles_for(rows);
     if (tiles == 1)
-        hipLaunchKernelGGL((absorb_kernel<1, 1>), dim3(kLatent / 16, heads, (rows + 15) / 16), dim3(64), 0,
+        hipLaunchKernelGGL((absorb_kernel<1, 1>), dim3(heads, kLatent / 16, (rows + 15) / 16), dim3(64), 0,
                            ctx->stream, ap);
     else if (tiles == 2)
-        hipLaunchKernelGGL((absorb_kernel<2, 1>), dim3(kLatent / 16, heads, (rows + 31) / 32), dim3(64), 0,
+        hipLaunchKernelGGL((absorb_kernel<2, 1>), dim3(heads, kLatent / 16, (rows + 31) / 32), dim3(64), 0,
                            ctx->stream, ap);
     else
-        hipLaunchKernelGGL((absorb_kernel<kMaxTiles, 4>), dim3(kLatent / 64, heads, (rows + 63) / 64), dim3(64), 0,
+        hipLaunchKernelGGL((absorb_kernel<kMaxTiles, 4>), dim3(heads, kLatent / 64, (rows + 63) / 64), dim3(64), 0,
                            ctx->stream, ap);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, "absorb_kernel launch");
@@ -400,7 +408,7 @@ int mla_project_out(mla_ctx *ctx, const float *o, const void *w_uv, float *out, 
         return fail(ctx, MLA_ERR_INVALID_ARG, "o, w_uv and out must be 16-byte aligned");
     ProjectParams pp{o, static_cast<const uint16_t *>(w_uv), out, rows, heads, d_v};
     const int tiles = tiles_for(rows);
-    const dim3 grid(d_v / 16, heads, (rows + 16 * tiles - 1) / (16 * tiles));
+    const dim3 grid(heads, d_v / 16, (rows + 16 * tiles - 1) / (16 * tiles));
     if (tiles == 1)
         hipLaunchKernelGGL(project_kernel<1>, grid, dim3(64 * kProjectWaves), 0, ctx->stream, pp);
     else if (tiles == 2)

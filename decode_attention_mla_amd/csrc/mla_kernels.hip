@@ -77,7 +77,9 @@ constexpr int kMergePitch = kDv + 4;           // floats per merge row (bank spr
 constexpr int kMergeWaveFloats = 16 * kMergePitch;          // one wave's O: 33 KB
 static_assert(2 * kMergeWaveFloats * 4 + kWaves * 16 * 2 * 4 <= kStageBytes,
               "two waves' merge rows and the stats fit in one stage array");
-constexpr int kCombineChannels = 64;           // channels per combine workgroup
+constexpr int kCombineChannels = 32;           // channels per combine workgroup (64 and 128: slower)
+constexpr int kCombineQuads = kCombineChannels / 4;       // threads per head, one float4 each
+constexpr int kCombineThreads = 16 * kCombineQuads;      // 16 heads
 constexpr int kCombineBatch = 16;              // partials merged per round trip
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1135,13 +1137,13 @@ void mla_split_kernel(Params p) {
 
 // ------------------------------------------------------------- combine kernel
 
-// grid (batch, n_rb, 512 / kCombineChannels); 256 threads = 16 heads x 16 quads.
-__global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
+// grid (batch, n_rb, 512 / kCombineChannels); 16 heads x kCombineQuads threads.
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(Params p) {
     const int b = blockIdx.x;
     const int rb = blockIdx.y;
     const int lane = threadIdx.x & 63;
-    const int head = threadIdx.x >> 4;
-    const int c = blockIdx.z * kCombineChannels + 4 * (threadIdx.x & 15);
+    const int head = threadIdx.x / kCombineQuads;
+    const int c = blockIdx.z * kCombineChannels + 4 * (threadIdx.x % kCombineQuads);
 
     int64_t total, st_b, lp;
     line_position(p, b, lane, total, st_b, lp);
@@ -1153,7 +1155,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
     float *lrow = p.lse + ((int64_t)b * p.s_q + t) * p.heads + hh;
     if (lp == 0) {  // no key at all: defined empty result
         *reinterpret_cast<f32x4 *>(orow) = f32x4{0.f, 0.f, 0.f, 0.f};
-        if ((threadIdx.x & 15) == 0 && blockIdx.z == 0) *lrow = -INFINITY;
+        if (threadIdx.x % kCombineQuads == 0 && blockIdx.z == 0) *lrow = -INFINITY;
         return;
     }
     const int g_first = (int)(st_b / chunk);
@@ -1200,7 +1202,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(Params p) {
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     *reinterpret_cast<f32x4 *>(orow) = o * inv;
-    if ((threadIdx.x & 15) == 0 && blockIdx.z == 0)
+    if (threadIdx.x % kCombineQuads == 0 && blockIdx.z == 0)
         *lrow = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
@@ -1544,7 +1546,7 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t 
     if (need_combine) {
         LaunchTimer t_comb(ctx, 1);
         hipLaunchKernelGGL(mla_combine_kernel, dim3(p->batch, n_rb, kDv / kCombineChannels),
-                           dim3(kThreads), 0, ctx->stream, prm);
+                           dim3(kCombineThreads), 0, ctx->stream, prm);
         e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(ctx, e, "mla_combine_kernel launch");
         t_comb.done();

@@ -106,6 +106,36 @@ def test_project_out_exact_on_sampled_outputs():
             abs(Fraction(float(o[r, h, c])) * frac_bf16(w[h, e, c])) for c in range(512)))
 
 
+def test_project_out_abs_exact_on_sampled_outputs():
+    """sum_c |o w| (the scale of each projected output's rounding error)
+    equals the exact rational sum of the absolute products; inputs of both
+    signs, so a missing absolute value, a wrong head or a wrong axis shows."""
+    rng = np.random.default_rng(14)
+    rows, H, dv = 3, 3, 48
+    o = rng.standard_normal((rows, H, 512)).astype(np.float32)
+    w = rand_bf16(rng, (H, dv, 512), 0.05)
+    mag = steps.project_out_abs(o, w)
+    assert mag.shape == (rows, H, dv)
+    for _ in range(30):
+        r, h, e = int(rng.integers(rows)), int(rng.integers(H)), int(rng.integers(dv))
+        exact = sum(abs(Fraction(float(o[r, h, c])) * frac_bf16(w[h, e, c])) for c in range(512))
+        # 512 nonnegative terms: the float64 sum is within 512 ulps of it
+        assert abs(mag[r, h, e] - float(exact)) <= 512 * 2.0 ** -52 * float(exact)
+
+
+def test_project_out_abs_bounds_the_projection():
+    """|sum o w| <= sum |o w| (triangle inequality), with equality exactly
+    where every product has one sign: nonnegative o and w, or o negated."""
+    rng = np.random.default_rng(15)
+    o = rng.standard_normal((4, 2, 512)).astype(np.float32)
+    w = rand_bf16(rng, (2, 32, 512))
+    assert np.all(np.abs(steps.project_out(o, w)) <= steps.project_out_abs(o, w) * (1 + 1e-12))
+    wpos = w & np.uint16(0x7FFF)  # clear the sign bit: |w| in bf16
+    opos = np.abs(o)
+    assert np.allclose(steps.project_out(opos, wpos), steps.project_out_abs(o, w), rtol=1e-13, atol=0)
+    assert np.allclose(-steps.project_out(-opos, wpos), steps.project_out_abs(-o, w), rtol=1e-13, atol=0)
+
+
 def test_project_out_one_hot_and_identity():
     rng = np.random.default_rng(11)
     H, dv = 2, 128

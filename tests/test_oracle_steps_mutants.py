@@ -13,7 +13,8 @@ import pytest
 import test_oracle_steps as pins
 from oracle import steps
 
-ORIG = {name: getattr(steps, name) for name in ("absorb_q", "project_out", "append_kv", "f64_to_bf16_bits")}
+ORIG = {name: getattr(steps, name)
+        for name in ("absorb_q", "project_out", "project_out_abs", "append_kv", "f64_to_bf16_bits")}
 
 
 def absorb_wrong_head(q_nope, q_rope, w_uk):
@@ -48,6 +49,20 @@ def project_in_fp32(o, w_uv):
     return ORIG["project_out"](o, w_uv).astype(np.float32).astype(np.float64)
 
 
+def project_abs_signed_weights(o, w_uv):
+    # the absolute value taken of o only
+    return np.einsum("rhc,hec->rhe", np.abs(np.asarray(o, dtype=np.float64)), steps.bf16_bits_to_f64(w_uv))
+
+
+def project_abs_of_sum(o, w_uv):
+    # |sum o w| instead of sum |o w|
+    return np.abs(ORIG["project_out"](o, w_uv))
+
+
+def project_abs_wrong_head(o, w_uv):
+    return ORIG["project_out_abs"](o, np.roll(w_uv, 1, axis=0))
+
+
 def append_shifted(kv, block_table, seqlens, new_rows):
     return ORIG["append_kv"](kv, block_table, np.asarray(seqlens) - 1, new_rows)
 
@@ -76,6 +91,9 @@ MUTANTS = {
     "project_wrong_head": ("project_out", project_wrong_head),
     "project_channel_dropped": ("project_out", project_channel_dropped),
     "project_in_fp32": ("project_out", project_in_fp32),
+    "project_abs_signed_weights": ("project_out_abs", project_abs_signed_weights),
+    "project_abs_of_sum": ("project_out_abs", project_abs_of_sum),
+    "project_abs_wrong_head": ("project_out_abs", project_abs_wrong_head),
     "append_shifted": ("append_kv", append_shifted),
     "append_tokens_reversed": ("append_kv", append_tokens_reversed),
     "round_truncating": ("f64_to_bf16_bits", round_truncating),

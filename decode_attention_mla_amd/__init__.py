@@ -181,39 +181,102 @@ class Context:
             pass
 
 
+def _need(name, t, dtype, shape=None, ndim=None):
+    """dtype, dense layout and shape of one tensor argument (None in `shape`
+    matches any size).  Checked before anything reaches the library: the C
+    ABI takes bare pointers, so these are the only bounds checks a wrong
+    shape meets."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, is {t.dtype}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise TypeError(f"{name} must have {ndim} dimensions, has {t.dim()}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(d) != w for d, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+            raise TypeError(f"{name} must have shape {want}, has {list(t.shape)}")
+
+
+def _on_one_device(**tensors):
+    """Every tensor on the same GPU (checked after the shapes)."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise TypeError(f"{name} must be a CUDA tensor (is on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise TypeError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _cache_layout(kv_cache, block_table, batch, kv_capacity):
+    """(page_size, kv_capacity, num_pages, max_pages) of a contiguous cache
+    [B', cap, 576] (B' >= batch) or a paged pool [P, page, 576] with a block
+    table [B', max_pages] (B' >= batch), checked against the batch."""
+    import torch
+
+    _need("kv_cache", kv_cache, torch.bfloat16, (None, None, HEAD_DIM_QK))
+    if block_table is None:
+        cap = int(kv_cache.shape[1]) if kv_capacity is None else int(kv_capacity)
+        if cap < 1 or cap > kv_cache.shape[1]:
+            raise TypeError(f"kv_capacity {cap} outside [1, {kv_cache.shape[1]}] (rows of kv_cache)")
+        if batch * cap * HEAD_DIM_QK > kv_cache.numel():
+            raise TypeError(f"kv_cache holds {kv_cache.numel() // HEAD_DIM_QK} rows, "
+                            f"{batch} sequences of capacity {cap} need {batch * cap}")
+        return 0, cap, 0, 0
+    if kv_capacity is not None:
+        raise TypeError("kv_capacity applies to the contiguous layout only")
+    _need("block_table", block_table, torch.int32, ndim=2)
+    if block_table.shape[0] < batch:
+        raise TypeError(f"block_table has {block_table.shape[0]} rows for {batch} sequences")
+    return int(kv_cache.shape[1]), 0, int(kv_cache.shape[0]), int(block_table.shape[1])
+
+
+def _host_lengths(seqlens_host, batch):
+    if seqlens_host is None:
+        return None
+    h = np.ascontiguousarray(seqlens_host, dtype=np.int32).reshape(-1)
+    if h.shape[0] < batch:
+        raise TypeError(f"seqlens_host has {h.shape[0]} entries for {batch} sequences")
+    return h[:batch]
+
+
 def mla_decode(ctx: Context, q, kv_cache, block_table, seqlens, scale: float, out=None, lse=None,
                seqlens_host: Optional[np.ndarray] = None, kv_capacity: Optional[int] = None):
     """Run mla_decode on torch tensors (device memory on ctx's device).
 
-    q [B, s_q, H, 576] bf16; kv_cache contiguous [B, cap, 576] or paged pool
-    [P, page, 576] bf16; block_table None or [B, max_pages] int32; seqlens
-    [B] int32 on the device; out [B, s_q, H, 512] fp32 and lse [B, s_q, H]
-    fp32 are allocated when not given.  Returns (out, lse).
+    q [B, s_q, H, 576] bf16; kv_cache contiguous [B', cap, 576] (B' >= B) or
+    paged pool [P, page, 576] bf16; block_table None or [B', max_pages]
+    int32; seqlens [>= B] int32 on the device; out [B, s_q, H, 512] fp32 and
+    lse [B, s_q, H] fp32 are allocated when not given.  kv_capacity
+    (contiguous only) overrides the per-sequence row stride, at most
+    kv_cache.shape[1].  Returns (out, lse).  Every shape is checked before
+    the call: a mismatch raises TypeError and launches nothing.
     """
     import torch
 
-    B, s_q, H, dqk = q.shape
+    _need("q", q, torch.bfloat16, (None, None, None, HEAD_DIM_QK))
+    B, s_q, H, dqk = (int(x) for x in q.shape)
+    page_size, cap, num_pages, max_pages = _cache_layout(kv_cache, block_table, B, kv_capacity)
+    _need("seqlens", seqlens, torch.int32, ndim=1)
+    if seqlens.shape[0] < B:
+        raise TypeError(f"seqlens has {seqlens.shape[0]} entries for {B} sequences")
+    host = _host_lengths(seqlens_host, B)
+    if out is not None:
+        _need("out", out, torch.float32, (B, s_q, H, HEAD_DIM_V))
+    if lse is not None:
+        _need("lse", lse, torch.float32, (B, s_q, H))
+    _on_one_device(q=q, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens, out=out, lse=lse)
     if out is None:
         out = torch.empty((B, s_q, H, HEAD_DIM_V), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q.device)
-    for name, t, dt in (("q", q, torch.bfloat16), ("kv_cache", kv_cache, torch.bfloat16),
-                        ("seqlens", seqlens, torch.int32), ("out", out, torch.float32),
-                        ("lse", lse, torch.float32)):
-        if t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
-            raise TypeError(f"{name} must be a contiguous {dt} CUDA tensor")
-    if block_table is None:
-        page_size, num_pages, max_pages = 0, 0, 0
-        cap = kv_cache.shape[1] if kv_capacity is None else kv_capacity
-        bt_ptr = None
-    else:
-        if block_table.dtype != torch.int32 or not block_table.is_contiguous():
-            raise TypeError("block_table must be a contiguous int32 CUDA tensor")
-        page_size, num_pages, max_pages = kv_cache.shape[1], kv_cache.shape[0], block_table.shape[1]
-        cap = 0
-        bt_ptr = block_table.data_ptr()
-    pr, keep = make_problem(B, s_q, H, page_size, cap, num_pages, max_pages, seqlens_host)
+    pr, keep = make_problem(B, s_q, H, page_size, cap, num_pages, max_pages, host)
     pr.head_dim_qk = dqk
+    bt_ptr = None if block_table is None else block_table.data_ptr()
     rc = load().mla_decode(ctx.handle, q.data_ptr(), kv_cache.data_ptr(), bt_ptr,
                            seqlens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
                            ctypes.byref(pr))
@@ -222,38 +285,27 @@ def mla_decode(ctx: Context, q, kv_cache, block_table, seqlens, scale: float, ou
     return out, lse
 
 
-def _need(name, t, dtype, ndim=None):
-    import torch
-
-    if t.dtype != dtype or not t.is_contiguous() or t.device.type != "cuda":
-        raise TypeError(f"{name} must be a contiguous {dtype} CUDA tensor")
-    if ndim is not None and t.dim() != ndim:
-        raise TypeError(f"{name} must have {ndim} dimensions, has {t.dim()}")
-
-
 def mla_append_kv(ctx: Context, new_rows, kv_cache, block_table, seqlens,
                   seqlens_host: Optional[np.ndarray] = None, kv_capacity: Optional[int] = None):
     """Write the latent rows of the new tokens into the cache, in place.
 
     new_rows [B, s_q, 576] bf16; kv_cache, block_table and seqlens as for
     ``mla_decode`` (seqlens are the lengths including the new tokens).
-    Returns kv_cache.
+    Returns kv_cache.  Shapes are checked as for ``mla_decode``.
     """
     import torch
 
-    _need("new_rows", new_rows, torch.bfloat16, 3)
-    _need("kv_cache", kv_cache, torch.bfloat16, 3)
-    _need("seqlens", seqlens, torch.int32, 1)
-    B, s_q, dqk = new_rows.shape
-    if block_table is None:
-        page_size, num_pages, max_pages, bt_ptr = 0, 0, 0, None
-        cap = kv_cache.shape[1] if kv_capacity is None else kv_capacity
-    else:
-        _need("block_table", block_table, torch.int32, 2)
-        page_size, num_pages, max_pages = kv_cache.shape[1], kv_cache.shape[0], block_table.shape[1]
-        cap, bt_ptr = 0, block_table.data_ptr()
-    pr, keep = make_problem(B, s_q, 1, page_size, cap, num_pages, max_pages, seqlens_host)
+    _need("new_rows", new_rows, torch.bfloat16, (None, None, HEAD_DIM_QK))
+    B, s_q, dqk = (int(x) for x in new_rows.shape)
+    page_size, cap, num_pages, max_pages = _cache_layout(kv_cache, block_table, B, kv_capacity)
+    _need("seqlens", seqlens, torch.int32, ndim=1)
+    if seqlens.shape[0] < B:
+        raise TypeError(f"seqlens has {seqlens.shape[0]} entries for {B} sequences")
+    host = _host_lengths(seqlens_host, B)
+    _on_one_device(new_rows=new_rows, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens)
+    pr, keep = make_problem(B, s_q, 1, page_size, cap, num_pages, max_pages, host)
     pr.head_dim_qk = dqk
+    bt_ptr = None if block_table is None else block_table.data_ptr()
     rc = load().mla_append_kv(ctx.handle, new_rows.data_ptr(), kv_cache.data_ptr(), bt_ptr,
                               seqlens.data_ptr(), ctypes.byref(pr))
     del keep
@@ -266,19 +318,18 @@ def mla_absorb_q(ctx: Context, q_nope, q_rope, w_uk, q_out=None):
     q_rope [..., H, 64] (bf16) and w_uk [H, 512, d_nope] bf16."""
     import torch
 
+    _need("w_uk", w_uk, torch.bfloat16, (None, HEAD_DIM_V, None))
+    H, lat, d_nope = (int(x) for x in w_uk.shape)
     _need("q_nope", q_nope, torch.bfloat16)
-    _need("q_rope", q_rope, torch.bfloat16)
-    _need("w_uk", w_uk, torch.bfloat16, 3)
-    H, lat, d_nope = w_uk.shape
-    lead = q_nope.shape[:-2]
-    if q_nope.shape[-2:] != (H, d_nope) or q_rope.shape != (*lead, H, HEAD_DIM_QK - HEAD_DIM_V):
-        raise TypeError("q_nope / q_rope shapes do not match w_uk")
+    lead = tuple(int(x) for x in q_nope.shape[:-2])
+    _need("q_nope", q_nope, torch.bfloat16, (*lead, H, d_nope))
+    _need("q_rope", q_rope, torch.bfloat16, (*lead, H, HEAD_DIM_QK - HEAD_DIM_V))
     rows = int(np.prod(lead)) if len(lead) else 1
+    if q_out is not None:
+        _need("q_out", q_out, torch.bfloat16, (*lead, H, HEAD_DIM_QK))
+    _on_one_device(q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, q_out=q_out)
     if q_out is None:
         q_out = torch.empty((*lead, H, HEAD_DIM_QK), dtype=torch.bfloat16, device=q_nope.device)
-    _need("q_out", q_out, torch.bfloat16)
-    if q_out.numel() != rows * H * HEAD_DIM_QK:
-        raise TypeError("q_out has the wrong size")
     _check(load().mla_absorb_q(ctx.handle, q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(),
                                q_out.data_ptr(), rows, H, d_nope), ctx.handle)
     return q_out
@@ -289,18 +340,17 @@ def mla_project_out(ctx: Context, o, w_uv, out=None):
     output o [..., H, 512] fp32 and w_uv [H, d_v, 512] bf16."""
     import torch
 
+    _need("w_uv", w_uv, torch.bfloat16, (None, None, HEAD_DIM_V))
+    H, d_v, lat = (int(x) for x in w_uv.shape)
     _need("o", o, torch.float32)
-    _need("w_uv", w_uv, torch.bfloat16, 3)
-    H, d_v, lat = w_uv.shape
-    lead = o.shape[:-2]
-    if o.shape[-2:] != (H, lat):
-        raise TypeError("o shape does not match w_uv")
+    lead = tuple(int(x) for x in o.shape[:-2])
+    _need("o", o, torch.float32, (*lead, H, lat))
     rows = int(np.prod(lead)) if len(lead) else 1
+    if out is not None:
+        _need("out", out, torch.float32, (*lead, H, d_v))
+    _on_one_device(o=o, w_uv=w_uv, out=out)
     if out is None:
         out = torch.empty((*lead, H, d_v), dtype=torch.float32, device=o.device)
-    _need("out", out, torch.float32)
-    if out.numel() != rows * H * d_v:
-        raise TypeError("out has the wrong size")
     _check(load().mla_project_out(ctx.handle, o.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
                                   rows, H, d_v), ctx.handle)
     return out

@@ -37,8 +37,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV HBM GB/s (% of peak) + µs/call, MLA decode bs16 ctx64K 16 heads"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("decode_attention_mla_amd/csrc/mla_kernels.hip", "decode_attention_mla_amd/csrc/context.h",
-                  "decode_attention_mla_amd/csrc/plan.h", "include/mla_decode.h")
+# The split and combine kernels and their launch configuration (the host side
+# of the C ABI lives elsewhere and does not change what the counters see).
+KERNEL_SOURCES = ("decode_attention_mla_amd/csrc/mla_kernels.hip", "decode_attention_mla_amd/csrc/plan.h",
+                  "decode_attention_mla_amd/csrc/launch.h")
 
 
 def kernel_source_hash() -> str:
@@ -335,6 +337,167 @@ def mla_steps(args) -> int:
     return 0
 
 
+# ----------------------------------------------------------- counter passes
+
+SQ_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+               "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+
+
+def _rocprof_pass(counters, bench_args, out_dir, timeout_s, reuse=False):
+    """One rocprofv3 counter pass over a child bench.py run; returns
+    {kernel name: {counter: mean per dispatch}} and the command line.  With
+    `reuse`, the raw output already in out_dir is read instead."""
+    import csv
+    import subprocess
+
+    cmd = ["rocprofv3", "--pmc", *counters, "-f", "csv", "-d", out_dir, "-o", "run", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *bench_args]
+    if not reuse:
+        os.makedirs(out_dir, exist_ok=True)
+        env = dict(os.environ, TMPDIR="/tmp")
+        print(f"[counters] {' '.join(cmd)}", file=sys.stderr, flush=True)
+        r = subprocess.run(["timeout", "-s", "KILL", str(timeout_s), *cmd], cwd="/tmp", env=env,
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"counter pass failed ({r.returncode}): {r.stderr[-2000:]}")
+    sums, counts = {}, {}
+    for root, _, files in os.walk(out_dir):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, fn)) as f:
+                for row in csv.DictReader(f):
+                    k = row["Kernel_Name"]
+                    c = row["Counter_Name"]
+                    key = (k, c, row.get("Dispatch_Id", ""))
+                    sums[key] = sums.get(key, 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (k, c, _), v in sums.items():
+        per.setdefault(k, {}).setdefault(c, []).append(v)
+    res = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    shown = " ".join(cmd).replace(out_dir, "<out>").replace(sys.executable, "python3").replace(ROOT, "/root/repo")
+    return res, f"cd /tmp && {shown}"
+
+
+def _kernel_entry(res, prefix):
+    for k, v in res.items():
+        if k.lstrip().startswith(prefix) or prefix in k:
+            return k, v
+    return None, {}
+
+
+def collect_counters(args) -> int:
+    """Counter passes for the split kernel of each named workload, each in a
+    run of its own (FETCH_SIZE, WRITE_SIZE, then the SQ counters), plus the
+    plain 1 GiB copy that calibrates the byte counters.  Writes
+    profiles/traffic_mla_split_<workload>.{json,md} and
+    profiles/counters_mla_split_<workload>.json, keyed by the kernel source
+    hash so that bench.py uses them only while the kernels are unchanged."""
+    import subprocess
+
+    rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                         text=True).stdout.strip() or "unknown"
+    sha = kernel_source_hash()
+    base = os.path.join(args.counters_dir, "pass")
+    n_pass = [0]
+
+    def run(counters, bench_args):
+        n_pass[0] += 1
+        return _rocprof_pass(counters, bench_args, f"{base}{n_pass[0]}", args.counters_timeout,
+                             reuse=args.counters_reuse)
+
+    cal_f, cmd_cf = run(["FETCH_SIZE"], ["--calibrate-copy", "--steps", "5"])
+    cal_w, cmd_cw = run(["WRITE_SIZE"], ["--calibrate-copy", "--steps", "5"])
+    _, cf = _kernel_entry(cal_f, "copyBuffer")
+    _, cw = _kernel_entry(cal_w, "copyBuffer")
+    copy_bytes = 1 << 30
+    fetch_factor = copy_bytes / (cf["FETCH_SIZE"] * 1024)
+    write_factor = copy_bytes / (cw["WRITE_SIZE"] * 1024)
+    for name in args.collect_counters.split(","):
+        import workloads as wl
+
+        w = wl.WORKLOADS[name]
+        kv_bytes = int(wl.draw_seqlens(w).astype("int64").sum()) * wl.D_QK * 2
+        wargs = ["--workload", name, "--settle-s", "0", "--steps", "5", "--warmup", "2", "--no-cpu-baseline"]
+        rf, cmd_f = run(["FETCH_SIZE"], wargs)
+        rw, cmd_w = run(["WRITE_SIZE"], wargs)
+        rs, cmd_s = run(list(SQ_COUNTERS), wargs)
+        ks, f = _kernel_entry(rf, "mla_split_kernel")
+        _, wv = _kernel_entry(rw, "mla_split_kernel")
+        _, sq = _kernel_entry(rs, "mla_split_kernel")
+        kc, fc = _kernel_entry(rf, "mla_combine_kernel")
+        _, wc = _kernel_entry(rw, "mla_combine_kernel")
+        fetch_b = int(round(f["FETCH_SIZE"] * 1024 * fetch_factor))
+        write_b = int(round(wv["WRITE_SIZE"] * 1024 * write_factor))
+        cmds = [cmd_f, cmd_cf, cmd_w, cmd_cw]
+        rec = {"kernel": "mla_split_kernel", "workload": name, "kernel_source_sha256": sha, "revision": rev,
+               "fetch_kib_per_dispatch": f["FETCH_SIZE"], "write_kib_per_dispatch": wv["WRITE_SIZE"],
+               "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
+                                    "fetch_kib": cf["FETCH_SIZE"], "write_kib": cw["WRITE_SIZE"],
+                                    "fetch_factor": fetch_factor, "write_factor": write_factor},
+               "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+               "bytes_per_launch": fetch_b + write_b, "algorithmic_kv_bytes": kv_bytes,
+               "fetch_over_algorithmic": fetch_b / kv_bytes, "commands": cmds}
+        if kc:
+            rec["combine_kernel"] = {"fetch_bytes": int(round(fc.get("FETCH_SIZE", 0) * 1024 * fetch_factor)),
+                                     "write_bytes": int(round(wc.get("WRITE_SIZE", 0) * 1024 * write_factor))}
+        prof = args.profiles_out
+        os.makedirs(prof, exist_ok=True)
+        with open(os.path.join(prof, f"traffic_mla_split_{name}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        busy_cycles = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        gui = sq.get("GRBM_GUI_ACTIVE", 0.0)
+        mfma_busy = 100.0 * busy_cycles / (SIMDS * gui / 8) if gui else None
+        crec = {"kernel": "mla_split_kernel", "workload": name, "kernel_source_sha256": sha, "revision": rev,
+                "counters_per_dispatch": sq, "mfma_busy_pct": mfma_busy,
+                "mfma_busy_definition": "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8)",
+                "command": cmd_s}
+        with open(os.path.join(prof, f"counters_mla_split_{name}.json"), "w") as fh:
+            json.dump(crec, fh, indent=1)
+            fh.write("\n")
+        lines = [f"# HBM traffic: mla_split_kernel, {name}", "",
+                 f"Source revision {rev} (kernel source sha256 {sha[:16]}...). Counters in their own runs "
+                 "(one counter group per run), written by `bench.py --collect-counters`:", "", "```",
+                 *cmds, cmd_s, "```", "",
+                 f"Calibration: a plain 1 GiB device copy (`bench.py --calibrate-copy`) reads FETCH_SIZE = "
+                 f"{cf['FETCH_SIZE']:,.1f} KiB and WRITE_SIZE = {cw['WRITE_SIZE']:,.1f} KiB per dispatch for "
+                 f"1,048,576 KiB moved each way: factors {fetch_factor:.4f} (fetch) and {write_factor:.4f} (write).",
+                 "", "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch bytes (calibrated) | write bytes (calibrated) |",
+                 "|---|---|---|---|---|",
+                 f"| mla_split_kernel | {f['FETCH_SIZE']:,.1f} | {wv['WRITE_SIZE']:,.1f} | {fetch_b:,} | {write_b:,} |"]
+        if kc:
+            lines.append(f"| mla_combine_kernel | {fc.get('FETCH_SIZE', 0):,.1f} | {wc.get('WRITE_SIZE', 0):,.1f} | "
+                         f"{rec['combine_kernel']['fetch_bytes']:,} | {rec['combine_kernel']['write_bytes']:,} |")
+        lines += ["", f"Algorithmic KV bytes per split launch: {kv_bytes:,}; fetched / algorithmic = "
+                  f"{fetch_b / kv_bytes:.4f}.", "",
+                  "SQ counters of the split kernel, mean per dispatch:", "", "| counter | value |", "|---|---|"]
+        lines += [f"| {c} | {v:,.0f} |" for c, v in sorted(sq.items())]
+        if mfma_busy is not None:
+            lines += ["", f"MFMA busy: {mfma_busy:.2f}% of SIMD time "
+                      "(SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8))."]
+        with open(os.path.join(prof, f"traffic_mla_split_{name}.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(json.dumps({"mode": "collect-counters", "workload": name, "fetch_over_algorithmic":
+                          round(fetch_b / kv_bytes, 4), "write_bytes": write_b, "mfma_busy_pct":
+                          None if mfma_busy is None else round(mfma_busy, 2)}), flush=True)
+    return 0
+
+
+def stored_mfma_busy(workload: str):
+    """MFMA busy % of the split kernel from committed SQ counters taken on
+    this exact kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_mla_split_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("mfma_busy_pct")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -360,12 +523,25 @@ def main() -> int:
     ap.add_argument("--step-shape", default="16,1,16", help="B,s_q,H of --mla-steps")
     ap.add_argument("--splits", type=int, default=0, help="key ranges per launch (0: library default)")
     ap.add_argument("--min-chunk", type=int, default=0, help="smallest key range (0: library default)")
+    ap.add_argument("--collect-counters", default="",
+                    help="comma-separated workloads: run the rocprofv3 counter passes of their split kernel "
+                         "(each pass a child run) and write profiles/traffic_* and profiles/counters_*")
+    ap.add_argument("--counters-dir", default=os.path.join(ROOT, "gpurun_out", "counters"),
+                    help="where the counter passes write their raw output")
+    ap.add_argument("--counters-timeout", type=int, default=300, help="seconds per counter pass")
+    ap.add_argument("--counters-reuse", action="store_true",
+                    help="read the raw output of earlier counter passes in --counters-dir instead of running them")
+    ap.add_argument("--profiles-out", default=os.path.join(ROOT, "profiles"),
+                    help="where --collect-counters writes its summaries")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library runs on a single MI355X "
               "(no collectives); use --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.collect_counters:
+        return collect_counters(args)  # before this process touches the GPU
 
     import numpy as np
     import torch
@@ -479,6 +655,8 @@ def main() -> int:
     }
     if traffic_rec is not None and traffic is None:
         res["roofline"]["traffic_note"] = "counters were taken on another kernel source"
+    busy = stored_mfma_busy(name)
+    res["roofline"]["mfma_busy_pct"] = None if busy is None else round(busy, 2)
 
     if not args.no_cpu_baseline:
         import oracle

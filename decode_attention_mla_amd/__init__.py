@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.mla_ctx_create.argtypes = [ctypes.POINTER(P), P]
     lib.mla_ctx_destroy.argtypes = [P]
     lib.mla_ctx_reserve.argtypes = [P, i32, i32]
+    lib.mla_workspace_size.argtypes = [P, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_ctx_set_workspace.argtypes = [P, P, ctypes.c_size_t]
     lib.mla_ctx_set_option.argtypes = [P, ctypes.c_int, i64]
     lib.mla_last_error.argtypes = [P]
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -91,6 +93,7 @@ def load() -> ctypes.CDLL:
     lib.mla_project_out.argtypes = [P, P, P, P, i32, i32, i32]
     lib.mla_version.restype = ctypes.c_char_p
     for name in ("mla_ctx_create", "mla_ctx_destroy", "mla_ctx_reserve", "mla_ctx_set_option",
+                 "mla_workspace_size", "mla_ctx_set_workspace",
                  "mla_decode", "mla_validate", "mla_plan", "mla_ctx_kernel_times",
                  "mla_append_kv", "mla_absorb_q", "mla_project_out"):
         getattr(lib, name).restype = ctypes.c_int
@@ -153,9 +156,40 @@ class Context:
         handle = ctypes.c_void_p()
         _check(lib.mla_ctx_create(ctypes.byref(handle), ctypes.c_void_p(stream.cuda_stream)))
         self.handle = handle
+        self.workspace = None  # a caller's workspace tensor, kept alive while set
 
     def reserve(self, s_q: int, num_heads: int) -> None:
         _check(load().mla_ctx_reserve(self.handle, s_q, num_heads), self.handle)
+
+    def workspace_size(self, s_q: int, num_heads: int) -> int:
+        """Bytes of device workspace mla_decode needs for up to s_q tokens and
+        num_heads heads (with the current split option)."""
+        n = ctypes.c_size_t(0)
+        _check(load().mla_workspace_size(self.handle, s_q, num_heads, ctypes.byref(n)))
+        return n.value
+
+    def set_workspace(self, buf) -> None:
+        """Use `buf` (a CUDA tensor on the context's device, 256-byte
+        aligned) as the split workspace; None returns to a workspace the
+        library allocates.  The tensor is kept alive while it is set."""
+        if buf is None:
+            _check(load().mla_ctx_set_workspace(self.handle, None, 0), self.handle)
+            self.workspace = None
+            return
+        if not buf.is_contiguous() or buf.device.type != "cuda":
+            raise TypeError("the workspace must be a contiguous CUDA tensor")
+        nbytes = buf.numel() * buf.element_size()
+        _check(load().mla_ctx_set_workspace(self.handle, buf.data_ptr(), nbytes), self.handle)
+        self.workspace = buf
+
+    def allocate_workspace(self, s_q: int, num_heads: int):
+        """Allocate the workspace for up to s_q tokens and num_heads heads as
+        a torch tensor on the current device, set it, and return it."""
+        import torch
+
+        buf = torch.empty(self.workspace_size(s_q, num_heads), dtype=torch.uint8, device="cuda")
+        self.set_workspace(buf)
+        return buf
 
     def set_option(self, option: int, value: int) -> None:
         _check(load().mla_ctx_set_option(self.handle, option, value), self.handle)

@@ -1,8 +1,7 @@
 """Build the gfx950 MLA decode library in-tree with hipcc.
 
 ``python -m decode_attention_mla_amd.build`` (or ``build()``) always
-recompiles ``csrc/mla_kernels.hip`` and ``csrc/mla_steps.hip`` into
-``_lib/libmla_decode.so``.
+recompiles every source under ``csrc/`` into ``_lib/libmla_decode.so``.
 """
 from __future__ import annotations
 
@@ -13,7 +12,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "mla_kernels.hip")         # the attention kernels
-SRCS = [SRC, os.path.join(PKG, "csrc", "mla_steps.hip")]  # every source of the library
+STEPS_SRC = os.path.join(PKG, "csrc", "mla_steps.hip")     # the MLA steps around them
+API_SRC = os.path.join(PKG, "csrc", "mla_api.cpp")         # host side of the C ABI
+SRCS = [SRC, STEPS_SRC, API_SRC]                           # every source of the library
 LIB = os.path.join(PKG, "_lib", "libmla_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -19,8 +19,15 @@ struct mla_ctx {
     int64_t opt_splits = 0;
     int64_t opt_min_chunk = mla::kDefaultMinChunk;
     bool timing = false;
+    // Split workspace: either the library's own (allocated on first use or
+    // by mla_ctx_reserve, grown by allocating a larger one) or a caller's
+    // buffer (mla_ctx_set_workspace).  A replaced buffer of the library's
+    // own is kept until the context is destroyed, so that work already
+    // enqueued or captured into a graph never sees it freed.
     void *ws = nullptr;
     size_t ws_bytes = 0;
+    bool ws_caller = false;
+    std::vector<void *> ws_retired;
     std::string err;
     // Event pairs around recorded launches: kind 0 = split, 1 = combine.
     struct Timed {

@@ -52,7 +52,7 @@
 #include <utility>
 #include <vector>
 
-#include "context.h"
+#include "launch.h"
 #include "mla_decode.h"
 #include "plan.h"
 
@@ -1208,277 +1208,27 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(Params p) 
 
 }  // namespace mla
 
-// =================================================================== host side
+// ======================================================= launch configuration
 
-namespace {
+namespace mla {
 
-using mla_host::fail;
-using mla_host::hip_fail;
-
-bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
-
-int check(mla_ctx *ctx, const void *q, const void *kv, const int32_t *block_table,
-          const int32_t *seqlens, float scale, const float *out, const float *lse,
-          const mla_problem *p) {
-    if (!p) return fail(ctx, MLA_ERR_INVALID_ARG, "problem description is NULL");
-    if (!q || !kv || !seqlens || !out || !lse)
-        return fail(ctx, MLA_ERR_INVALID_ARG, "q, kv_cache, seqlens, out and lse must be non-NULL");
-    if (p->batch < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", p->batch);
-    if (p->s_q < 1) return fail(ctx, MLA_ERR_INVALID_ARG, "s_q must be >= 1 (got %d)", p->s_q);
-    if (p->num_heads < 1 || p->num_heads % 16)
-        return fail(ctx, MLA_ERR_UNSUPPORTED, "num_heads must be a positive multiple of 16 (got %d)",
-                    p->num_heads);
-    if (p->head_dim_qk != MLA_HEAD_DIM_QK || p->head_dim_v != MLA_HEAD_DIM_V)
-        return fail(ctx, MLA_ERR_UNSUPPORTED, "head dims must be %d/%d (got %d/%d)", MLA_HEAD_DIM_QK,
-                    MLA_HEAD_DIM_V, p->head_dim_qk, p->head_dim_v);
-    if ((int64_t)p->s_q * p->num_heads > (1 << 20))
-        return fail(ctx, MLA_ERR_UNSUPPORTED, "s_q * num_heads too large");
-    if (!isfinite(scale)) return fail(ctx, MLA_ERR_INVALID_ARG, "scale must be finite");
-    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || ((uintptr_t)lse & 3))
-        return fail(ctx, MLA_ERR_INVALID_ARG,
-                    "q, kv_cache and out must be 16-byte aligned, lse 4-byte aligned");
-    int64_t capacity;
-    if (p->page_size == 0) {
-        if (block_table)
-            return fail(ctx, MLA_ERR_INVALID_ARG, "block_table given but page_size is 0 (contiguous)");
-        if (p->kv_capacity < 1 || p->kv_capacity > (int64_t)INT32_MAX)
-            return fail(ctx, MLA_ERR_INVALID_ARG, "kv_capacity must be in [1, 2^31) (got %lld)",
-                        (long long)p->kv_capacity);
-        capacity = p->kv_capacity;
-    } else {
-        if (p->page_size < 0 || p->page_size % MLA_KEY_BLOCK)
-            return fail(ctx, MLA_ERR_UNSUPPORTED, "page_size must be a positive multiple of %d (got %d)",
-                        MLA_KEY_BLOCK, p->page_size);
-        if (!block_table) return fail(ctx, MLA_ERR_INVALID_ARG, "paged layout needs a block_table");
-        if (p->num_pages < 1 || p->max_pages < 1)
-            return fail(ctx, MLA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
-        capacity = (int64_t)p->max_pages * p->page_size;
-        if (capacity > (int64_t)INT32_MAX)
-            return fail(ctx, MLA_ERR_INVALID_ARG, "max_pages * page_size must be < 2^31");
-    }
-    if (p->seqlens_host) {
-        for (int b = 0; b < p->batch; ++b) {
-            const int32_t L = p->seqlens_host[b];
-            if (L < p->s_q || (int64_t)L > capacity)
-                return fail(ctx, MLA_ERR_INVALID_ARG,
-                            "seqlens[%d] = %d outside [s_q = %d, capacity = %lld]", b, L, p->s_q,
-                            (long long)capacity);
-        }
-    }
-    return MLA_OK;
-}
-
-int64_t min_chunk_of(const mla_ctx *ctx) { return ctx->opt_min_chunk > 0 ? ctx->opt_min_chunk : mla::kDefaultMinChunk; }
-
-}  // namespace
-
-extern "C" {
-
-const char *mla_version(void) { return "mla_decode 0.1 gfx950"; }
-
-const char *mla_last_error(const mla_ctx *ctx) { return ctx ? ctx->err.c_str() : mla_host::thread_error().c_str(); }
-
-int mla_validate(const void *q, const void *kv_cache, const int32_t *block_table,
-                 const int32_t *seqlens, float scale, const float *out, const float *lse,
-                 const mla_problem *p) {
-    mla_host::thread_error().clear();
-    return check(nullptr, q, kv_cache, block_table, seqlens, scale, out, lse, p);
-}
-
-int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits, int64_t min_chunk,
-             mla_plan_segment *segs, int32_t max_segs, int32_t *n_segs, mla_plan_info *info) {
-    using namespace mla;
-    mla_host::thread_error().clear();
-    if (!seqlens_host || batch < 1 || num_splits < 1 || !n_segs)
-        return fail(nullptr, MLA_ERR_INVALID_ARG, "mla_plan: bad arguments");
-    int64_t total = 0;
-    for (int b = 0; b < batch; ++b) total += padded_len(seqlens_host[b] < 0 ? 0 : seqlens_host[b]);
-    const int64_t chunk = plan_chunk(total, num_splits, min_chunk);
-    int32_t count = 0, split_seqs = 0;
-    int64_t st = 0;
-    for (int b = 0; b < batch; ++b) {
-        const int32_t L = seqlens_host[b] < 0 ? 0 : seqlens_host[b];
-        const int64_t lp = padded_len(L);
-        if (lp == 0) continue;
-        const int g_first = (int)(st / chunk), g_last = (int)((st + lp - 1) / chunk);
-        if (g_first != g_last) ++split_seqs;
-        for (int g = g_first; g <= g_last; ++g) {
-            const int64_t gs = (int64_t)g * chunk, ge = std::min(gs + chunk, total);
-            if (segs && count < max_segs) {
-                mla_plan_segment &s = segs[count];
-                s.group = g;
-                s.seq = b;
-                s.key_begin = (int32_t)(std::max(gs, st) - st);
-                s.key_end = (int32_t)std::min<int64_t>(std::min(ge, st + lp) - st, L);
-                s.slot = g_first == g_last ? -1 : segment_slot(g, st, chunk);
-            }
-            ++count;
-        }
-        st += lp;
-    }
-    *n_segs = count;
-    if (info) {
-        info->chunk = chunk;
-        info->total_keys = total;
-        info->active_groups = (int32_t)((total + chunk - 1) / chunk);
-        info->split_sequences = split_seqs;
-    }
-    if (segs && count > max_segs)
-        return fail(nullptr, MLA_ERR_INVALID_ARG, "mla_plan: %d segments, room for %d", count, max_segs);
-    return MLA_OK;
-}
-
-int mla_ctx_create(mla_ctx **out_ctx, void *stream) {
-    mla_host::thread_error().clear();
-    if (!out_ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx out-pointer is NULL");
-    *out_ctx = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(nullptr, e, "hipDeviceGetAttribute");
-    mla_ctx *ctx = new (std::nothrow) mla_ctx;
-    if (!ctx) return fail(nullptr, MLA_ERR_WORKSPACE, "out of host memory");
-    ctx->stream = (hipStream_t)stream;
-    ctx->device = dev;
-    ctx->cu_count = cus > 0 ? cus : 256;
-    *out_ctx = ctx;
-    return MLA_OK;
-}
-
-int mla_ctx_destroy(mla_ctx *ctx) {
-    if (!ctx) return MLA_OK;
-    int rc = MLA_OK;
-    if (ctx->ws) {
-        hipError_t e = hipStreamSynchronize(ctx->stream);
-        if (e == hipSuccess) e = hipFree(ctx->ws);
-        if (e != hipSuccess) rc = hip_fail(nullptr, e, "mla_ctx_destroy");
-    }
-    for (auto &t : ctx->timed) {
-        (void)hipEventDestroy(t.start);
-        (void)hipEventDestroy(t.stop);
-    }
-    for (auto e : ctx->spare) (void)hipEventDestroy(e);
-    delete ctx;
-    return rc;
-}
-
-int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value) {
-    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
-    switch (option) {
-    case MLA_OPT_NUM_SPLITS:
-        if (value < 0 || value > (1 << 20)) return fail(ctx, MLA_ERR_INVALID_ARG, "bad split count");
-        ctx->opt_splits = value;
-        return MLA_OK;
-    case MLA_OPT_MIN_CHUNK:
-        if (value < 0 || value > ((int64_t)1 << 31)) return fail(ctx, MLA_ERR_INVALID_ARG, "bad min chunk");
-        ctx->opt_min_chunk = value ? value : mla::kDefaultMinChunk;
-        return MLA_OK;
-    case MLA_OPT_KERNEL_TIMING:
-        ctx->timing = value != 0;
-        return MLA_OK;
-    default:
-        return fail(ctx, MLA_ERR_INVALID_ARG, "unknown option %d", option);
-    }
-}
-
-}  // extern "C"
-
-namespace {
-
-hipError_t take_event(mla_ctx *ctx, hipEvent_t *e) {
-    if (!ctx->spare.empty()) {
-        *e = ctx->spare.back();
-        ctx->spare.pop_back();
-        return hipSuccess;
-    }
-    return hipEventCreate(e);
-}
-
-// Record an event pair around one launch when timing is on.
-struct LaunchTimer {
-    mla_ctx *ctx;
-    int kind;
-    hipEvent_t start = nullptr, stop = nullptr;
-    LaunchTimer(mla_ctx *c, int k) : ctx(c), kind(k) {
-        if (!ctx->timing) return;
-        if (take_event(ctx, &start) != hipSuccess || take_event(ctx, &stop) != hipSuccess) {
-            ctx->timing = false;
-            return;
-        }
-        (void)hipEventRecord(start, ctx->stream);
-    }
-    void done() {
-        if (!start) return;
-        (void)hipEventRecord(stop, ctx->stream);
-        ctx->timed.push_back({start, stop, kind});
-    }
-};
-
-// Row-block groups per launch: groups of four (and a last group of three)
-// go to one launch, a last group of one or two to a second launch after it.
-// The key ranges are sized so that the larger launch fills the GPU once.
 int groups_per_launch(int n_rb) {
-    const int rem = n_rb % mla::kWaves;
-    const int full = n_rb / mla::kWaves + (rem == 3 ? 1 : 0);
+    const int rem = n_rb % kWaves;
+    const int full = n_rb / kWaves + (rem == 3 ? 1 : 0);
     return std::max(full, (rem == 1 || rem == 2) ? 1 : 0);
 }
 
-int splits_for(const mla_ctx *ctx, int n_rb) {
-    if (ctx->opt_splits > 0) return (int)ctx->opt_splits;
-    return std::max(1, ctx->cu_count / groups_per_launch(n_rb));
-}
+int default_splits(int cu_count, int n_rb) { return std::max(1, cu_count / groups_per_launch(n_rb)); }
 
 size_t workspace_bytes(int splits, int n_rb) {
     const size_t rows = (size_t)2 * splits * n_rb * 16;
-    return rows * (mla::kDv + 1) * sizeof(float) + 256;
+    return rows * (kDv + 1) * sizeof(float) + 256;
 }
 
-int ensure_workspace(mla_ctx *ctx, size_t need) {
-    if (ctx->ws_bytes >= need) return MLA_OK;
-    if (ctx->ws) {
-        hipError_t e = hipStreamSynchronize(ctx->stream);
-        if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
-        e = hipFree(ctx->ws);
-        ctx->ws = nullptr;
-        ctx->ws_bytes = 0;
-        if (e != hipSuccess) return hip_fail(ctx, e, "hipFree");
-    }
-    hipError_t e = hipMalloc(&ctx->ws, need);
-    if (e != hipSuccess) {
-        ctx->ws = nullptr;
-        return fail(ctx, MLA_ERR_WORKSPACE, "hipMalloc(%zu): %s", need, hipGetErrorString(e));
-    }
-    ctx->ws_bytes = need;
-    return MLA_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads) {
-    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
-    if (s_q < 1 || num_heads < 16 || num_heads % 16)
-        return fail(ctx, MLA_ERR_INVALID_ARG, "bad s_q / num_heads");
-    const int n_rb = s_q * num_heads / 16;
-    return ensure_workspace(ctx, workspace_bytes(splits_for(ctx, n_rb), n_rb));
-}
-
-int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t *block_table,
-               const int32_t *seqlens, float scale, float *out, float *lse, const mla_problem *p) {
-    using namespace mla;
-    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
-    ctx->err.clear();
-    int rc = check(ctx, q, kv_cache, block_table, seqlens, scale, out, lse, p);
-    if (rc != MLA_OK) return rc;
-
+hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, void *ws, const void *q,
+                         const void *kv_cache, const int32_t *block_table, const int32_t *seqlens, float scale,
+                         float *out, float *lse, const mla_problem *p, LaunchEvents *ev, const char **what) {
     const int n_rb = p->s_q * p->num_heads / 16;
-    const int splits = splits_for(ctx, n_rb);
-    rc = ensure_workspace(ctx, workspace_bytes(splits, n_rb));
-    if (rc != MLA_OK) return rc;
-
     Params prm;
     prm.q = static_cast<const uint16_t *>(q);
     prm.kv = static_cast<const uint16_t *>(kv_cache);
@@ -1486,12 +1236,12 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t 
     prm.seqlens = seqlens;
     prm.out = out;
     prm.lse = lse;
-    prm.part_o = static_cast<float *>(ctx->ws);
+    prm.part_o = static_cast<float *>(ws);
     prm.part_lse = prm.part_o + (size_t)2 * splits * n_rb * 16 * kDv;
     prm.kv_capacity = p->page_size ? 0 : p->kv_capacity;
     prm.num_pages = p->page_size ? p->num_pages : 0;
     prm.capacity = p->page_size ? (int64_t)p->max_pages * p->page_size : p->kv_capacity;
-    prm.min_chunk = min_chunk_of(ctx);
+    prm.min_chunk = min_chunk;
     prm.batch = p->batch;
     prm.s_q = p->s_q;
     prm.heads = p->num_heads;
@@ -1525,57 +1275,43 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t 
     // one.  Each launch covers groups y0 .. y0 + gridDim.y - 1.
     const int rem = n_rb % kWaves;
     const int full = n_rb / kWaves + (rem == 3 ? 1 : 0);
-    LaunchTimer t_split(ctx, 0);
+    if (ev) (void)hipEventRecord(ev->split_start, stream);
     hipError_t e = hipSuccess;
     if (full > 0) {
         prm.y0 = 0;
-        hipLaunchKernelGGL(mla_split_kernel<kOneGroup>, dim3(grid_x, full), dim3(kThreads), 0, ctx->stream, prm);
+        hipLaunchKernelGGL(mla_split_kernel<kOneGroup>, dim3(grid_x, full), dim3(kThreads), 0, stream, prm);
         e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(ctx, e, "mla_split_kernel launch");
+        if (e != hipSuccess) {
+            *what = "mla_split_kernel launch";
+            return e;
+        }
     }
     if (rem == 1 || rem == 2) {
         prm.y0 = n_rb / kWaves;
         if (rem == 1)
-            hipLaunchKernelGGL(mla_split_kernel<kOneBlock>, dim3(grid_x, 1), dim3(kThreads), 0, ctx->stream, prm);
+            hipLaunchKernelGGL(mla_split_kernel<kOneBlock>, dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
         else
-            hipLaunchKernelGGL(mla_split_kernel<kTwoGroups>, dim3(grid_x, 1), dim3(kThreads), 0, ctx->stream, prm);
+            hipLaunchKernelGGL(mla_split_kernel<kTwoGroups>, dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
         e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(ctx, e, "mla_split_kernel launch");
+        if (e != hipSuccess) {
+            *what = "mla_split_kernel launch";
+            return e;
+        }
     }
-    t_split.done();
+    if (ev) (void)hipEventRecord(ev->split_stop, stream);
+    if (ev) ev->combine_ran = need_combine;
     if (need_combine) {
-        LaunchTimer t_comb(ctx, 1);
+        if (ev) (void)hipEventRecord(ev->comb_start, stream);
         hipLaunchKernelGGL(mla_combine_kernel, dim3(p->batch, n_rb, kDv / kCombineChannels),
-                           dim3(kCombineThreads), 0, ctx->stream, prm);
+                           dim3(kCombineThreads), 0, stream, prm);
         e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(ctx, e, "mla_combine_kernel launch");
-        t_comb.done();
+        if (e != hipSuccess) {
+            *what = "mla_combine_kernel launch";
+            return e;
+        }
+        if (ev) (void)hipEventRecord(ev->comb_stop, stream);
     }
-    return MLA_OK;
+        return hipSuccess;
 }
 
-int mla_ctx_kernel_times(mla_ctx *ctx, double *split_ms, int64_t *split_launches,
-                         double *combine_ms, int64_t *combine_launches) {
-    if (!ctx) return fail(nullptr, MLA_ERR_INVALID_ARG, "ctx is NULL");
-    hipError_t e = hipStreamSynchronize(ctx->stream);
-    if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
-    double ms[2] = {0.0, 0.0};
-    int64_t n[2] = {0, 0};
-    for (auto &t : ctx->timed) {
-        float v = 0.f;
-        e = hipEventElapsedTime(&v, t.start, t.stop);
-        if (e != hipSuccess) return hip_fail(ctx, e, "hipEventElapsedTime");
-        ms[t.kind] += v;
-        n[t.kind] += 1;
-        ctx->spare.push_back(t.start);
-        ctx->spare.push_back(t.stop);
-    }
-    ctx->timed.clear();
-    if (split_ms) *split_ms = ms[0];
-    if (split_launches) *split_launches = n[0];
-    if (combine_ms) *combine_ms = ms[1];
-    if (combine_launches) *combine_launches = n[1];
-    return MLA_OK;
-}
-
-}  // extern "C"
+}  // namespace mla

@@ -21,7 +21,9 @@
  *    failure mla_last_error() describes the first problem found.
  *  - Argument checks are host code and run before any HIP call.
  *  - mla_decode only enqueues work on the context's stream: it never blocks
- *    the host and, once the context holds enough workspace, never allocates.
+ *    the host.  With a caller's workspace (mla_ctx_set_workspace), or once
+ *    the context's own workspace is large enough (mla_ctx_reserve), it never
+ *    allocates either.
  *  - A context is used by one host thread at a time.
  */
 #ifndef MLA_DECODE_H
@@ -38,7 +40,7 @@ typedef enum {
     MLA_OK = 0,
     MLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, bad length */
     MLA_ERR_UNSUPPORTED = -2, /* well-formed but outside what the kernels implement */
-    MLA_ERR_WORKSPACE = -3,   /* workspace allocation failed */
+    MLA_ERR_WORKSPACE = -3,   /* workspace too small, or its allocation failed */
     MLA_ERR_HIP = -4          /* a HIP runtime call failed */
 } mla_status;
 
@@ -86,20 +88,54 @@ typedef struct mla_ctx mla_ctx;
 
 /*
  * Create a context bound to the current HIP device and to `stream` (a
- * hipStream_t; NULL means the default stream).  The context owns the split
- * workspace.  Returns MLA_OK and sets *ctx, or an error code.
+ * hipStream_t; NULL means the default stream).  Until it is given a
+ * caller's workspace the context allocates its own on first use.  Returns
+ * MLA_OK and sets *ctx, or an error code.
  */
 int mla_ctx_create(mla_ctx **ctx, void *stream);
 
-/* Release the context and its workspace (synchronizes its stream first).
- * NULL is accepted. */
+/* Release the context and the workspace it allocated itself (synchronizes
+ * its stream first).  A caller's workspace is not touched.  NULL is
+ * accepted. */
 int mla_ctx_destroy(mla_ctx *ctx);
 
 /*
- * Make sure the workspace holds the split partials for problems with up to
- * `s_q` tokens and `num_heads` heads, so that later mla_decode calls of that
- * size do not allocate.  Allocates with hipMalloc; synchronizes the stream
- * when it replaces a smaller workspace.
+ * Device workspace mla_decode needs on `ctx` for problems of up to `s_q`
+ * query tokens and `num_heads` heads: the split partials (normalized O and
+ * LSE of every key range that ends inside a sequence), 2 * splits *
+ * (s_q * num_heads / 16) * 16 * 513 floats plus 256 bytes, where splits is
+ * the key-range count of one launch (the device's CU count over the
+ * row-block groups that share a launch, or MLA_OPT_NUM_SPLITS).  It does not
+ * depend on the batch or the lengths.  Changing MLA_OPT_NUM_SPLITS changes
+ * it.  Writes the byte count to *bytes.
+ */
+int mla_workspace_size(const mla_ctx *ctx, int32_t s_q, int32_t num_heads, size_t *bytes);
+
+/*
+ * Give the context a workspace owned by the caller: `bytes` bytes of device
+ * memory at `dev_ptr`, 256-byte aligned, on the context's device.  From then
+ * on mla_decode uses it for the split partials and never allocates, frees
+ * or synchronizes; a problem that needs more than `bytes` (see
+ * mla_workspace_size) is refused with MLA_ERR_WORKSPACE before anything is
+ * enqueued.  The buffer holds no state between calls; it must stay valid
+ * until the work enqueued with it (and any graph captured with it) has run,
+ * and two contexts must not share it while their work can overlap.  The
+ * context's own workspace, if any, is kept until mla_ctx_destroy (work
+ * already enqueued may use it).  dev_ptr = NULL returns to a workspace the
+ * context allocates itself.  No HIP call is made.
+ */
+int mla_ctx_set_workspace(mla_ctx *ctx, void *dev_ptr, size_t bytes);
+
+/*
+ * Make sure the context's own workspace holds the split partials for
+ * problems with up to `s_q` tokens and `num_heads` heads, so that later
+ * mla_decode calls of that size do not allocate (needed before capturing
+ * mla_decode into a graph).  Allocates with hipMalloc when it must grow; the
+ * smaller buffer it replaces is freed only by mla_ctx_destroy, so work
+ * already enqueued or captured keeps a valid buffer and no synchronization
+ * is needed.  With a caller's workspace set it only checks that it is large
+ * enough (MLA_ERR_WORKSPACE if not).  Growing while the context's stream is
+ * being captured is refused (MLA_ERR_WORKSPACE).
  */
 int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads);
 

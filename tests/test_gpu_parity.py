@@ -1,9 +1,9 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
 
 Bar (fp32 outputs): O RMSE <= 1e-4, O max-abs <= 1e-3, LSE max-abs <= 1e-4.
-Small shapes are checked element by element on every row; the full-size
-workloads on every row where the oracle is quick and on sampled sequences
-otherwise, in the default launch configuration that bench.py times.
+Every case is checked element by element on every row, the full-size
+workloads included (in the default launch configuration that bench.py
+times).
 """
 import sys
 
@@ -215,27 +215,21 @@ def test_bitwise_repeatable(ctx):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("name,rows", [
-    ("mla_bs1_ctx512", None),
-    ("mla_bs16_ctx4096", None),
-    ("mla_bs16_ctx65536", [0, 15]),
-    ("mla_bs64_ragged1k_32k_paged64", [0, 17, 63]),
-    ("mla_bs32_sq4_ctx16384", [0, 31]),
-])
-def test_workload_full_size(ctx, name, rows):
+@pytest.mark.parametrize("name", sorted(wl.WORKLOADS))
+def test_workload_full_size(ctx, name):
+    """Each workload at its full size, in the launch configuration bench.py
+    times: every output element of every row against the oracle."""
     import torch
 
-    announce(f"workload {name} rows={rows}")
+    announce(f"workload {name}, every row")
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w, poison=True)
     o, l = run_gpu(ctx, inp)
     torch.cuda.empty_cache()
-    ro, rl = oracle_of(inp, rows)
-    sel = slice(None) if rows is None else rows
-    compare(o[sel], l[sel], ro, rl, name)
-    # every row: finite, and the LSE of an N(0,1) context lies near
-    # ln(L) + |scale q|^2 / 2 (the Gaussian tilt law of the inputs)
-    assert np.isfinite(o).all() and np.isfinite(l).all()
+    ro, rl = oracle_of(inp)
+    compare(o, l, ro, rl, name)
+    # and the LSE of an N(0,1) context lies near ln(L) + |scale q|^2 / 2
+    # (the Gaussian tilt law of the inputs)
     a2 = (wl.bf16_bits_to_f32(inp.q).astype(np.float64) * inp.scale) ** 2
     vis = inp.seqlens[:, None].astype(np.float64) - w.s_q + 1 + np.arange(w.s_q)[None, :]
     law = np.log(vis)[:, :, None] + a2.sum(-1) / 2

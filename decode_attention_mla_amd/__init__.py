@@ -91,9 +91,12 @@ def load() -> ctypes.CDLL:
     lib.mla_append_kv.argtypes = [P, P, P, P, P, ctypes.POINTER(Problem)]
     lib.mla_absorb_q.argtypes = [P, P, P, P, P, i32, i32, i32]
     lib.mla_project_out.argtypes = [P, P, P, P, i32, i32, i32]
+    lib.mla_decode_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.POINTER(Problem)]
+    lib.mla_noalloc_scratch_bytes.argtypes = []
+    lib.mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.mla_version.restype = ctypes.c_char_p
     for name in ("mla_ctx_create", "mla_ctx_destroy", "mla_ctx_reserve", "mla_ctx_set_option",
-                 "mla_workspace_size", "mla_ctx_set_workspace",
+                 "mla_workspace_size", "mla_ctx_set_workspace", "mla_decode_noalloc",
                  "mla_decode", "mla_validate", "mla_plan", "mla_ctx_kernel_times",
                  "mla_append_kv", "mla_absorb_q", "mla_project_out"):
         getattr(lib, name).restype = ctypes.c_int
@@ -317,6 +320,44 @@ def mla_decode(ctx: Context, q, kv_cache, block_table, seqlens, scale: float, ou
     del keep
     _check(rc, ctx.handle)
     return out, lse
+
+
+def mla_decode_noalloc(q, kv_cache, block_table, seqlens, scale: float, out, lse,
+                       seqlens_host: Optional[np.ndarray] = None, kv_capacity: Optional[int] = None,
+                       stream=None):
+    """mla_decode without a context and without any allocation: the split
+    partials go to the library's static scratch array.  out and lse must be
+    given (shapes as for ``mla_decode``); `stream` defaults to torch's
+    current stream.  Returns (out, lse)."""
+    import torch
+
+    _need("q", q, torch.bfloat16, (None, None, None, HEAD_DIM_QK))
+    B, s_q, H, dqk = (int(x) for x in q.shape)
+    page_size, cap, num_pages, max_pages = _cache_layout(kv_cache, block_table, B, kv_capacity)
+    _need("seqlens", seqlens, torch.int32, ndim=1)
+    if seqlens.shape[0] < B:
+        raise TypeError(f"seqlens has {seqlens.shape[0]} entries for {B} sequences")
+    host = _host_lengths(seqlens_host, B)
+    if out is None or lse is None:
+        raise TypeError("mla_decode_noalloc writes into the caller's out and lse: pass both")
+    _need("out", out, torch.float32, (B, s_q, H, HEAD_DIM_V))
+    _need("lse", lse, torch.float32, (B, s_q, H))
+    _on_one_device(q=q, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens, out=out, lse=lse)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    pr, keep = make_problem(B, s_q, H, page_size, cap, num_pages, max_pages, host)
+    pr.head_dim_qk = dqk
+    bt_ptr = None if block_table is None else block_table.data_ptr()
+    rc = load().mla_decode_noalloc(ctypes.c_void_p(stream.cuda_stream), q.data_ptr(), kv_cache.data_ptr(),
+                                   bt_ptr, seqlens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
+                                   ctypes.byref(pr))
+    del keep
+    _check(rc)
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().mla_noalloc_scratch_bytes())
 
 
 def mla_append_kv(ctx: Context, new_rows, kv_cache, block_table, seqlens,

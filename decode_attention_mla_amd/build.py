@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "mla_kernels.hip")         # the attention kernels
 STEPS_SRC = os.path.join(PKG, "csrc", "mla_steps.hip")     # the MLA steps around them
 API_SRC = os.path.join(PKG, "csrc", "mla_api.cpp")         # host side of the C ABI
-SRCS = [SRC, STEPS_SRC, API_SRC]                           # every source of the library
+NOALLOC_SRC = os.path.join(PKG, "csrc", "mla_noalloc.hip")  # the entry point that allocates nothing
+SRCS = [SRC, STEPS_SRC, API_SRC, NOALLOC_SRC]              # every source of the library
 LIB = os.path.join(PKG, "_lib", "libmla_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -203,6 +203,28 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache,
                float *out, float *lse, const mla_problem *p);
 
 /*
+ * mla_decode for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid device allocation.
+ * Same arguments, checks and result as mla_decode (on the stream `stream`, a
+ * hipStream_t, NULL for the default stream), but with no context: nothing
+ * is allocated, freed or synchronized.  The split partials go to a static
+ * scratch array of mla_noalloc_scratch_bytes() bytes (64.1 MiB) that every
+ * GPU the library runs on holds until the process ends; its address is
+ * looked up on the first call on each device.  The default split plan is
+ * used when its partials fit the array, else the largest key-range count
+ * that fits (the same result up to rounding); a problem of more than 16,384
+ * query rows (s_q * num_heads) does not fit at all and is refused with
+ * MLA_ERR_WORKSPACE before anything is enqueued.  All calls on one GPU share
+ * its array: calls that may overlap on one GPU (several streams or threads)
+ * race.  Errors go to mla_last_error(NULL).
+ */
+int mla_decode_noalloc(void *stream, const void *q, const void *kv_cache, const int32_t *block_table,
+                       const int32_t *seqlens, float scale, float *out, float *lse, const mla_problem *p);
+
+/* Size of the static scratch array of mla_decode_noalloc, in bytes. */
+size_t mla_noalloc_scratch_bytes(void);
+
+/*
  * Host-only argument check of mla_decode (the same checks, in the same
  * order, without a context or any HIP call).  Pointers are only tested for
  * NULL and alignment.  The message goes to mla_last_error(NULL).

@@ -3,7 +3,9 @@ reads, the query loads into accumulation registers).  The compiler takes an
 asm statement's outputs as written when the statement ends, so every such
 statement must wait for its own loads before it ends.  This test builds the
 gfx950 assembly with the library's own flags and checks exactly that, for
-every inline-asm block of the split kernel (CPU only: hipcc cross-compiles).
+every inline-asm block of the split kernels and of the MLA steps' kernels,
+and that no kernel of either source spills to scratch or uses packed fp32
+arithmetic (CPU only: hipcc cross-compiles).
 """
 import re
 import subprocess
@@ -18,13 +20,22 @@ LDS_LOAD = re.compile(r"^ds_read")
 VMEM_LOAD = re.compile(r"^(global_load|buffer_load|flat_load)")
 
 
+def device_asm(tmp_path_factory, src, name):
+    out = tmp_path_factory.mktemp("isa") / name
+    flags = [f for f in libbuild.FLAGS if f not in ("-fPIC", "-shared")]
+    subprocess.run([libbuild.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), src],
+                   check=True, capture_output=True)
+    return out.read_text().split("\n")
+
+
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "mla.s"
-    flags = [f for f in libbuild.FLAGS if f not in ("-fPIC", "-shared")]
-    subprocess.run([libbuild.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out),
-                    libbuild.SRC], check=True, capture_output=True)
-    return out.read_text().split("\n")
+    return device_asm(tmp_path_factory, libbuild.SRC, "mla.s")
+
+
+@pytest.fixture(scope="module")
+def steps_asm(tmp_path_factory):
+    return device_asm(tmp_path_factory, libbuild.STEPS_SRC, "steps.s")
 
 
 # Every instance of the split kernel: one row block per workgroup, two key
@@ -75,8 +86,43 @@ def test_inline_asm_loads_wait_in_their_own_statement(asm, name):
     assert checked > 0, "no inline-asm loads found: the check is vacuous"
 
 
+def kernel_names(asm):
+    names = []
+    for line in asm:
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            names.append(m.group(1))
+    return names
+
+
+def check_clean(body, name):
+    text = "\n".join(body)
+    assert "scratch_" not in text, f"{name} spills to scratch"
+    for op in ("v_pk_mul_f32", "v_pk_add_f32", "v_pk_fma_f32"):
+        assert op not in text, f"{name} uses {op}"
+
+
 @pytest.mark.parametrize("name", SPLIT_KERNELS)
 def test_no_scratch_in_the_split_kernel(asm, name):
-    body = "\n".join(kernel_body(asm, name))
-    assert "scratch_" not in body, "the split kernel spills to scratch"
-    assert "v_pk_mul_f32" not in body and "v_pk_add_f32" not in body and "v_pk_fma_f32" not in body
+    check_clean(kernel_body(asm, name), name)
+
+
+def test_every_device_function_is_clean(asm, steps_asm):
+    """No scratch and no packed fp32 arithmetic anywhere in the device code
+    of either source: the attention kernels (combine included) and the MLA
+    steps' kernels."""
+    names = 0
+    for code in (asm, steps_asm):
+        for name in kernel_names(code):
+            check_clean(kernel_body(code, name), name)
+            names += 1
+    assert names >= len(SPLIT_KERNELS) + 2 + 3, "kernels missing from the assembly"
+    assert any("mla_combine_kernel" in n for n in kernel_names(asm))
+    assert sum("absorb" in n or "project" in n or "append" in n for n in kernel_names(steps_asm)) >= 3
+
+
+def test_inline_asm_loads_wait_in_the_steps_kernels(steps_asm):
+    for name in kernel_names(steps_asm):
+        for ins in asm_blocks(kernel_body(steps_asm, name)):
+            if any(LDS_LOAD.match(i) or VMEM_LOAD.match(i) for i in ins):
+                assert ins[-1].startswith("s_waitcnt"), f"{name}: asm loads without a closing wait: {ins}"

@@ -342,6 +342,9 @@ def mla_steps(args) -> int:
 SQ_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
                "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
 SIMDS = 1024  # 256 CUs x 4 SIMDs
+# Raw L2-to-memory read requests, all, 32-byte, 128-byte ("bubble") and
+# those sent on to DRAM: FETCH_SIZE is computed from the first three.
+TCC_READ_REQUESTS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum")
 
 
 def _rocprof_pass(counters, bench_args, out_dir, timeout_s, reuse=False):
@@ -409,11 +412,17 @@ def collect_counters(args) -> int:
 
     cal_f, cmd_cf = run(["FETCH_SIZE"], ["--calibrate-copy", "--steps", "5"])
     cal_w, cmd_cw = run(["WRITE_SIZE"], ["--calibrate-copy", "--steps", "5"])
+    cal_r, cmd_cr = run(list(TCC_READ_REQUESTS), ["--calibrate-copy", "--steps", "5"])
     _, cf = _kernel_entry(cal_f, "copyBuffer")
     _, cw = _kernel_entry(cal_w, "copyBuffer")
+    _, cr = _kernel_entry(cal_r, "copyBuffer")
     copy_bytes = 1 << 30
     fetch_factor = copy_bytes / (cf["FETCH_SIZE"] * 1024)
     write_factor = copy_bytes / (cw["WRITE_SIZE"] * 1024)
+    # Bytes per read request, measured on the copy (all its requests are of
+    # one kind): the size that FETCH_SIZE's expression should have used.
+    copy_req = cr.get("TCC_EA0_RDREQ_sum", 0.0)
+    req_size = copy_bytes / copy_req if copy_req else None
     for name in args.collect_counters.split(","):
         import workloads as wl
 
@@ -423,7 +432,9 @@ def collect_counters(args) -> int:
         rf, cmd_f = run(["FETCH_SIZE"], wargs)
         rw, cmd_w = run(["WRITE_SIZE"], wargs)
         rs, cmd_s = run(list(SQ_COUNTERS), wargs)
+        rr, cmd_r = run(list(TCC_READ_REQUESTS), wargs)
         ks, f = _kernel_entry(rf, "mla_split_kernel")
+        _, rq = _kernel_entry(rr, "mla_split_kernel")
         _, wv = _kernel_entry(rw, "mla_split_kernel")
         _, sq = _kernel_entry(rs, "mla_split_kernel")
         kc, fc = _kernel_entry(rf, "mla_combine_kernel")
@@ -439,6 +450,14 @@ def collect_counters(args) -> int:
                "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
                "bytes_per_launch": fetch_b + write_b, "algorithmic_kv_bytes": kv_bytes,
                "fetch_over_algorithmic": fetch_b / kv_bytes, "commands": cmds}
+        if req_size:
+            n_req = rq.get("TCC_EA0_RDREQ_sum", 0.0)
+            rec["read_requests"] = {
+                "counters_per_dispatch": rq, "copy_counters_per_dispatch": cr,
+                "bytes_per_request_from_copy": req_size,
+                "request_bytes_per_launch": int(round(n_req * req_size)),
+                "request_bytes_over_algorithmic": n_req * req_size / kv_bytes,
+                "commands": [cmd_r, cmd_cr]}
         if kc:
             rec["combine_kernel"] = {"fetch_bytes": int(round(fc.get("FETCH_SIZE", 0) * 1024 * fetch_factor)),
                                      "write_bytes": int(round(wc.get("WRITE_SIZE", 0) * 1024 * write_factor))}
@@ -471,8 +490,19 @@ def collect_counters(args) -> int:
             lines.append(f"| mla_combine_kernel | {fc.get('FETCH_SIZE', 0):,.1f} | {wc.get('WRITE_SIZE', 0):,.1f} | "
                          f"{rec['combine_kernel']['fetch_bytes']:,} | {rec['combine_kernel']['write_bytes']:,} |")
         lines += ["", f"Algorithmic KV bytes per split launch: {kv_bytes:,}; fetched / algorithmic = "
-                  f"{fetch_b / kv_bytes:.4f}.", "",
-                  "SQ counters of the split kernel, mean per dispatch:", "", "| counter | value |", "|---|---|"]
+                  f"{fetch_b / kv_bytes:.4f}.", ""]
+        if "read_requests" in rec:
+            rr_ = rec["read_requests"]
+            lines += ["Check of the fetch factor with the raw L2-to-memory read requests (one more pass each):", "",
+                      "```", cmd_r, cmd_cr, "```", "",
+                      "| counter (per dispatch) | mla_split_kernel | 1 GiB copy |", "|---|---|---|"]
+            lines += [f"| {c} | {rq.get(c, 0.0):,.0f} | {cr.get(c, 0.0):,.0f} |" for c in TCC_READ_REQUESTS]
+            lines += ["", f"The copy reads 1 GiB in {copy_req:,.0f} requests: {req_size:.2f} B per request. "
+                      "FETCH_SIZE's expression counts 32 B for a 32-byte request, 128 B for a bubble and 64 B for "
+                      f"any other. At {req_size:.2f} B per request the split kernel's requests come to "
+                      f"{rr_['request_bytes_per_launch']:,} B per launch, "
+                      f"{rr_['request_bytes_over_algorithmic']:.4f} of the algorithmic bytes.", ""]
+        lines += ["SQ counters of the split kernel, mean per dispatch:", "", "| counter | value |", "|---|---|"]
         lines += [f"| {c} | {v:,.0f} |" for c, v in sorted(sq.items())]
         if mfma_busy is not None:
             lines += ["", f"MFMA busy: {mfma_busy:.2f}% of SIMD time "
@@ -482,6 +512,71 @@ def collect_counters(args) -> int:
         print(json.dumps({"mode": "collect-counters", "workload": name, "fetch_over_algorithmic":
                           round(fetch_b / kv_bytes, 4), "write_bytes": write_b, "mfma_busy_pct":
                           None if mfma_busy is None else round(mfma_busy, 2)}), flush=True)
+    return 0
+
+
+def trace_summary(args) -> int:
+    """A rocprofv3 kernel trace of bench.py's timed run of each named
+    workload (a child run), summarized per kernel into
+    profiles/mla_split_<workload>_kernel_trace.md."""
+    import csv
+    import subprocess
+
+    import workloads as wl
+
+    rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                         text=True).stdout.strip() or "unknown"
+    sha = kernel_source_hash()
+    for name in args.trace_summary.split(","):
+        w = wl.WORKLOADS[name]
+        kv_bytes = int(wl.draw_seqlens(w).astype("int64").sum()) * wl.D_QK * 2
+        out_dir = os.path.join(args.counters_dir, f"trace_{name}")
+        cmd = ["rocprofv3", "--kernel-trace", "--stats", "-f", "csv", "-d", out_dir, "-o", "run", "--",
+               sys.executable, os.path.join(ROOT, "bench.py"), "--workload", name, "--steps", "20",
+               "--warmup", "5", "--no-cpu-baseline"]
+        if not args.counters_reuse:
+            os.makedirs(out_dir, exist_ok=True)
+            print(f"[trace] {' '.join(cmd)}", file=sys.stderr, flush=True)
+            r = subprocess.run(["timeout", "-s", "KILL", str(args.counters_timeout), *cmd], cwd="/tmp",
+                               env=dict(os.environ, TMPDIR="/tmp"), capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"trace run failed ({r.returncode}): {r.stderr[-2000:]}")
+        rows = []
+        for root, _, files in os.walk(out_dir):
+            for fn in files:
+                if fn.endswith("kernel_stats.csv"):
+                    with open(os.path.join(root, fn)) as f:
+                        rows += list(csv.DictReader(f))
+        rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+        shown = " ".join(cmd).replace(out_dir, "<out>").replace(sys.executable, "python3").replace(ROOT, "/root/repo")
+        lines = [f"# Kernel trace: {name}", "",
+                 f"Source revision: {rev} (kernel source sha256 {sha[:16]}...), MI355X (gfx950), ROCm 7.2.", "",
+                 "Command:", "", "```", f"cd /tmp && {shown}", "```", "",
+                 "Every dispatch of the run is counted: the clock-settling steps (about one second), the warmup, "
+                 "the timed steps and the event-timed repeat.", "",
+                 "| kernel | calls | mean us | min us | max us | share |", "|---|---|---|---|---|---|"]
+        split_mean = None
+        for r in rows:
+            mean = float(r["AverageNs"]) / 1e3
+            lines.append(f"| {r['Name']} | {int(r['Calls'])} | {mean:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |")
+            if "mla_split_kernel" in r["Name"]:
+                calls = int(r["Calls"])
+                # several split launches per step (row-block groups): their sum per step
+                split_mean = (split_mean or 0.0) + mean * calls
+                split_calls = calls
+        if split_mean is not None:
+            groups = sum(1 for r in rows if "mla_split_kernel" in r["Name"])
+            per_step = split_mean / split_calls if groups == 1 else None
+            if per_step is not None:
+                lines += ["", f"KV bytes per launch (sum of L_b x 1152 B): {kv_bytes:,}; split kernel mean "
+                          f"{per_step:.2f} us -> {kv_bytes / per_step / 1e3:.1f} GB/s "
+                          f"({kv_bytes / per_step / 1e3 / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s)."]
+        os.makedirs(args.profiles_out, exist_ok=True)
+        with open(os.path.join(args.profiles_out, f"mla_split_{name}_kernel_trace.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(json.dumps({"mode": "trace-summary", "workload": name, "kernels": len(rows)}), flush=True)
     return 0
 
 
@@ -532,7 +627,10 @@ def main() -> int:
     ap.add_argument("--counters-reuse", action="store_true",
                     help="read the raw output of earlier counter passes in --counters-dir instead of running them")
     ap.add_argument("--profiles-out", default=os.path.join(ROOT, "profiles"),
-                    help="where --collect-counters writes its summaries")
+                    help="where --collect-counters and --trace-summary write their summaries")
+    ap.add_argument("--trace-summary", default="",
+                    help="comma-separated workloads: a rocprofv3 kernel trace of each one's bench run "
+                         "(a child run), summarized into profiles/mla_split_<workload>_kernel_trace.md")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -540,8 +638,13 @@ def main() -> int:
               "(no collectives); use --gpus 1.", file=sys.stderr)
         return 2
 
+    # the counter and trace runs are children started in /tmp
+    args.counters_dir = os.path.abspath(args.counters_dir)
+    args.profiles_out = os.path.abspath(args.profiles_out)
     if args.collect_counters:
         return collect_counters(args)  # before this process touches the GPU
+    if args.trace_summary:
+        return trace_summary(args)
 
     import numpy as np
     import torch
@@ -655,6 +758,13 @@ def main() -> int:
     }
     if traffic_rec is not None and traffic is None:
         res["roofline"]["traffic_note"] = "counters were taken on another kernel source"
+    if traffic is not None and "read_requests" in traffic_rec:
+        # the same reads counted as raw requests at the copy's bytes per request
+        rq = traffic_rec["read_requests"]
+        res["roofline"]["fetch_check"] = {
+            "request_bytes_per_launch": rq["request_bytes_per_launch"],
+            "bytes_per_request_from_copy": round(rq["bytes_per_request_from_copy"], 2),
+            "fetch_bytes_per_launch": traffic_rec["fetch_bytes_per_launch"]}
     busy = stored_mfma_busy(name)
     res["roofline"]["mfma_busy_pct"] = None if busy is None else round(busy, 2)
 

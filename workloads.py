@@ -54,7 +54,10 @@ class Workload:
         return float(np.float32(1.0 / math.sqrt(D_QK)))
 
 
-# The five shapes the bench and the parity tests use.
+# The shapes the bench, the counter runs and the parity tests use: the five
+# decode shapes at 16 heads per GPU, then the headline context at 64 and 128
+# heads (the 128-head model on two GPUs and on one; the same summary's
+# Problem Statement).
 WORKLOADS = {
     w.name: w
     for w in (
@@ -63,6 +66,8 @@ WORKLOADS = {
         Workload("mla_bs16_ctx65536", 16, 1, 16, 65536, 0, 1002),
         Workload("mla_bs64_ragged1k_32k_paged64", 64, 1, 16, (1024, 32768), 64, 1003),
         Workload("mla_bs32_sq4_ctx16384", 32, 4, 16, 16384, 0, 1004),
+        Workload("mla_bs16_h64_ctx65536", 16, 1, 64, 65536, 0, 1005),
+        Workload("mla_bs16_h128_ctx65536", 16, 1, 128, 65536, 0, 1006),
     )
 }
 HEADLINE = "mla_bs16_ctx65536"

@@ -556,23 +556,20 @@ def trace_summary(args) -> int:
                  "Every dispatch of the run is counted: the clock-settling steps (about one second), the warmup, "
                  "the timed steps and the event-timed repeat.", "",
                  "| kernel | calls | mean us | min us | max us | share |", "|---|---|---|---|---|---|"]
-        split_mean = None
+        split_rows = []
         for r in rows:
             mean = float(r["AverageNs"]) / 1e3
             lines.append(f"| {r['Name']} | {int(r['Calls'])} | {mean:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                          f"{float(r['MaxNs']) / 1e3:.2f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |")
             if "mla_split_kernel" in r["Name"]:
-                calls = int(r["Calls"])
-                # several split launches per step (row-block groups): their sum per step
-                split_mean = (split_mean or 0.0) + mean * calls
-                split_calls = calls
-        if split_mean is not None:
-            groups = sum(1 for r in rows if "mla_split_kernel" in r["Name"])
-            per_step = split_mean / split_calls if groups == 1 else None
-            if per_step is not None:
-                lines += ["", f"KV bytes per launch (sum of L_b x 1152 B): {kv_bytes:,}; split kernel mean "
-                          f"{per_step:.2f} us -> {kv_bytes / per_step / 1e3:.1f} GB/s "
-                          f"({kv_bytes / per_step / 1e3 / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s)."]
+                split_rows.append(mean)
+        # One split launch per step covers all the keys once (every workload
+        # here launches one instantiation once per step): bytes / its mean.
+        if len(split_rows) == 1:
+            mean = split_rows[0]
+            lines += ["", f"KV bytes per launch (sum of L_b x 1152 B): {kv_bytes:,}; split kernel mean "
+                      f"{mean:.2f} us -> {kv_bytes / mean / 1e3:.1f} GB/s "
+                      f"({kv_bytes / mean / 1e3 / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s)."]
         os.makedirs(args.profiles_out, exist_ok=True)
         with open(os.path.join(args.profiles_out, f"mla_split_{name}_kernel_trace.md"), "w") as fh:
             fh.write("\n".join(lines) + "\n")

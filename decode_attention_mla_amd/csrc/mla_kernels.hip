@@ -1137,6 +1137,51 @@ void mla_split_kernel(Params p) {
 
 // ------------------------------------------------------------- combine kernel
 
+// Online merge of a sequence's parts g_first .. g_first + n_parts - 1 for
+// one head and four channels, NB parts at a time: all loads of a batch are
+// issued before any is used, so a batch costs one round trip.  Returns the
+// log2-domain max M, the weight sum lsum and the weighted O sum o.
+template <int NB>
+__device__ inline void merge_parts(const Params &p, int rb, int head, int c, int g_first, int n_parts,
+                                   int64_t st_b, int64_t chunk, float &M, float &lsum, f32x4 &o) {
+    M = -INFINITY;
+    lsum = 0.f;
+    o = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < n_parts; k0 += NB) {
+        float lv[NB];
+        f32x4 ov[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int g = g_first + min(k0 + k, n_parts - 1);
+            const int64_t r = ((int64_t)segment_slot(g, st_b, chunk) * p.n_rb + rb) * 16 + head;
+            lv[k] = p.part_lse[r];
+            ov[k] = *reinterpret_cast<const f32x4 *>(p.part_o + r * kDv + c);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all loads of the batch are in flight before any use
+        float mb = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (k0 + k >= n_parts) lv[k] = -INFINITY;
+            mb = fmaxf(mb, lv[k]);
+        }
+        const float m_new = fmaxf(M, mb);
+        // Until some part holds a key every weight is 0; a finite reference
+        // then keeps exp2 away from -inf - -inf.  (No branch here: a branch
+        // on the LSEs would let the compiler sink the O loads below it.)
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(M - m_ref);
+        lsum *= alpha;
+        o *= alpha;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const float w = __builtin_amdgcn_exp2f(lv[k] - m_ref);  // 0 for -inf parts
+            lsum += w;
+            o += w * ov[k];
+        }
+        M = m_new;
+    }
+}
+
 // grid (batch, n_rb, 512 / kCombineChannels); 16 heads x kCombineQuads threads.
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(Params p) {
     const int b = blockIdx.x;
@@ -1162,44 +1207,17 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(Params p) 
     const int g_last = (int)((st_b + lp - 1) / chunk);
     if (g_first == g_last) return;  // finished inside one range by the split kernel
 
-    // Online merge over the parts, kCombineBatch at a time: all loads of a
-    // batch are issued before any is used, so a batch costs one round trip.
+    // Batches no wider than the parts of the sequence: a wider one would
+    // repeat the last part's loads.
     const int n_parts = g_last - g_first + 1;
-    float M = -INFINITY, lsum = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < n_parts; k0 += kCombineBatch) {
-        float lv[kCombineBatch];
-        f32x4 ov[kCombineBatch];
-#pragma unroll
-        for (int k = 0; k < kCombineBatch; ++k) {
-            const int g = g_first + min(k0 + k, n_parts - 1);
-            const int64_t r = ((int64_t)segment_slot(g, st_b, chunk) * p.n_rb + rb) * 16 + head;
-            lv[k] = p.part_lse[r];
-            ov[k] = *reinterpret_cast<const f32x4 *>(p.part_o + r * kDv + c);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // all loads of the batch are in flight before any use
-        float mb = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < kCombineBatch; ++k) {
-            if (k0 + k >= n_parts) lv[k] = -INFINITY;
-            mb = fmaxf(mb, lv[k]);
-        }
-        const float m_new = fmaxf(M, mb);
-        // Until some part holds a key every weight is 0; a finite reference
-        // then keeps exp2 away from -inf - -inf.  (No branch here: a branch
-        // on the LSEs would let the compiler sink the O loads below it.)
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(M - m_ref);
-        lsum *= alpha;
-        o *= alpha;
-#pragma unroll
-        for (int k = 0; k < kCombineBatch; ++k) {
-            const float w = __builtin_amdgcn_exp2f(lv[k] - m_ref);  // 0 for -inf parts
-            lsum += w;
-            o += w * ov[k];
-        }
-        M = m_new;
-    }
+    float M, lsum;
+    f32x4 o;
+    if (n_parts <= 4)
+        merge_parts<4>(p, rb, head, c, g_first, n_parts, st_b, chunk, M, lsum, o);
+    else if (n_parts <= 8)
+        merge_parts<8>(p, rb, head, c, g_first, n_parts, st_b, chunk, M, lsum, o);
+    else
+        merge_parts<kCombineBatch>(p, rb, head, c, g_first, n_parts, st_b, chunk, M, lsum, o);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     *reinterpret_cast<f32x4 *>(orow) = o * inv;
     if (threadIdx.x % kCombineQuads == 0 && blockIdx.z == 0)

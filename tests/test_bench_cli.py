@@ -46,3 +46,67 @@ def test_stored_traffic_matches_the_current_kernels():
 
     traffic, rec = bench.stored_traffic("mla_bs16_ctx65536")
     assert rec is not None and traffic is not None, "profiles/traffic_* are stale: re-take the counters"
+
+
+def _counter_csv(path, rows):
+    path.mkdir(parents=True, exist_ok=True)
+    lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    lines += [f"{d},{k},{c},{v}" for d, k, c, v in rows]
+    (path / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+
+
+def test_counter_summary_from_raw_output(tmp_path):
+    """--collect-counters on stored raw output (no GPU): the copy calibrates
+    both byte counters and the bytes per read request, and the split
+    kernel's request count is turned into bytes at that size."""
+    import json
+
+    copy, split = "__amd_rocclr_copyBuffer", "void mla::mla_split_kernel<0>(mla::Params)"
+    gib_kib = 1 << 20
+    d = tmp_path / "raw"
+    # the passes in the order bench.py runs them: the copy's three, then the workload's four
+    _counter_csv(d / "pass1", [(1, copy, "FETCH_SIZE", gib_kib / 2)])
+    _counter_csv(d / "pass2", [(1, copy, "WRITE_SIZE", gib_kib)])
+    _counter_csv(d / "pass3", [(1, copy, "TCC_EA0_RDREQ_sum", (1 << 30) // 128),
+                               (1, copy, "TCC_EA0_RDREQ_32B_sum", 0), (1, copy, "TCC_BUBBLE_sum", 0),
+                               (1, copy, "TCC_EA0_RDREQ_DRAM_sum", (1 << 30) // 128)])
+    kv = 512 * 1152  # the bs1 ctx512 workload's KV bytes
+    # two dispatches of the split kernel: the summary takes their mean
+    _counter_csv(d / "pass4", [(1, split, "FETCH_SIZE", kv / 2 / 1024), (2, split, "FETCH_SIZE", kv / 2 / 1024)])
+    _counter_csv(d / "pass5", [(1, split, "WRITE_SIZE", 256.0)])
+    _counter_csv(d / "pass6", [(1, split, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0), (1, split, "GRBM_GUI_ACTIVE", 80.0)])
+    _counter_csv(d / "pass7", [(1, split, "TCC_EA0_RDREQ_sum", kv // 128 + 10), (1, split, "TCC_EA0_RDREQ_32B_sum", 0),
+                               (1, split, "TCC_BUBBLE_sum", 0), (1, split, "TCC_EA0_RDREQ_DRAM_sum", kv // 128)])
+    prof = tmp_path / "prof"
+    r = run_bench("--collect-counters", "mla_bs1_ctx512", "--counters-reuse", "--counters-dir", str(d),
+                  "--profiles-out", str(prof))
+    assert r.returncode == 0, r.stderr
+    rec = json.loads((prof / "traffic_mla_split_mla_bs1_ctx512.json").read_text())
+    assert rec["copy_calibration"]["fetch_factor"] == 2.0 and rec["copy_calibration"]["write_factor"] == 1.0
+    assert rec["fetch_bytes_per_launch"] == kv and rec["write_bytes_per_launch"] == 256 * 1024
+    rq = rec["read_requests"]
+    assert rq["bytes_per_request_from_copy"] == 128.0
+    assert rq["request_bytes_per_launch"] == kv + 10 * 128
+    counters = json.loads((prof / "counters_mla_split_mla_bs1_ctx512.json").read_text())
+    assert counters["mfma_busy_pct"] == 100.0 * 1024 / (1024 * 80 / 8)
+    md = (prof / "traffic_mla_split_mla_bs1_ctx512.md").read_text()
+    assert "128.00 B per request" in md and "TCC_BUBBLE_sum" in md
+
+
+def test_trace_summary_from_raw_output(tmp_path):
+    """--trace-summary on a stored kernel_stats.csv (no GPU): one table row
+    per kernel and the split kernel's bandwidth from its mean duration."""
+    d = tmp_path / "raw" / "trace_mla_bs1_ctx512"
+    d.mkdir(parents=True)
+    (d / "run_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void mla::mla_split_kernel<0>(mla::Params)",10,100000,10000.0,90.9,9000,12000,100\n'
+        '"mla::mla_combine_kernel(mla::Params)",10,10000,1000.0,9.1,900,1200,10\n')
+    prof = tmp_path / "prof"
+    r = run_bench("--trace-summary", "mla_bs1_ctx512", "--counters-reuse", "--counters-dir",
+                  str(tmp_path / "raw"), "--profiles-out", str(prof))
+    assert r.returncode == 0, r.stderr
+    md = (prof / "mla_split_mla_bs1_ctx512_kernel_trace.md").read_text()
+    assert "| void mla::mla_split_kernel<0>(mla::Params) | 10 | 10.00 | 9.00 | 12.00 | 90.9% |" in md
+    # 589,824 B in 10 us
+    assert "split kernel mean 10.00 us -> 59.0 GB/s" in md

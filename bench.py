@@ -30,6 +30,7 @@ import json
 import math
 import os
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -618,7 +619,7 @@ def main() -> int:
     ap.add_argument("--collect-counters", default="",
                     help="comma-separated workloads: run the rocprofv3 counter passes of their split kernel "
                          "(each pass a child run) and write profiles/traffic_* and profiles/counters_*")
-    ap.add_argument("--counters-dir", default=os.path.join(ROOT, "gpurun_out", "counters"),
+    ap.add_argument("--counters-dir", default=os.path.join(tempfile.gettempdir(), "mla_decode_counters"),
                     help="where the counter passes write their raw output")
     ap.add_argument("--counters-timeout", type=int, default=300, help="seconds per counter pass")
     ap.add_argument("--counters-reuse", action="store_true",

@@ -121,6 +121,7 @@ def sweep(args) -> int:
     ctx.set_option(mla.MLA_OPT_NUM_SPLITS, args.splits)
     ctx.set_option(mla.MLA_OPT_MIN_CHUNK, args.min_chunk)
     scale = 1.0 / 24.0
+    results = []
     for B, s_q, H, L in points:
         gen.manual_seed(7000 + B * 131 + H * 17 + L)
         q = torch.randn((B, s_q, H, 576), generator=gen, device="cuda").to(torch.bfloat16)
@@ -159,18 +160,42 @@ def sweep(args) -> int:
         split_ms, n_split, comb_ms, n_comb = ctx.kernel_times()
         ctx.set_option(mla.MLA_OPT_KERNEL_TIMING, 0)
         split_us = split_ms * 1e3 / max(1, n_split)
-        print(json.dumps({"mode": "sweep", "batch": B, "s_q": s_q, "heads": H, "kv_len": L,
-                          "min_chunk": args.min_chunk or "default",
-                          "kv_bytes": kv_bytes, "us_per_call": round(us, 2),
-                          "GBps": round(kv_bytes / us / 1e3, 1),
-                          "split_us": round(split_us, 2),
-                          "split_GBps": round(kv_bytes / split_us / 1e3, 1),
-                          "split_frac_of_8TBps": round(kv_bytes / split_us / 1e3 / PEAK_HBM_GBS, 4),
-                          "combine_us": round(comb_ms * 1e3 / n_comb, 2) if n_comb else 0.0}), flush=True)
+        res = {"mode": "sweep", "batch": B, "s_q": s_q, "heads": H, "kv_len": L,
+               "min_chunk": args.min_chunk or "default",
+               "kv_bytes": kv_bytes, "us_per_call": round(us, 2),
+               "GBps": round(kv_bytes / us / 1e3, 1),
+               "split_us": round(split_us, 2),
+               "split_GBps": round(kv_bytes / split_us / 1e3, 1),
+               "split_frac_of_8TBps": round(kv_bytes / split_us / 1e3 / PEAK_HBM_GBS, 4),
+               "combine_us": round(comb_ms * 1e3 / n_comb, 2) if n_comb else 0.0}
+        results.append(res)
+        print(json.dumps(res), flush=True)
         del q, kv, copies, out, lse
         torch.cuda.empty_cache()
     ctx.close()
+    if not args.sweep_points:
+        write_sweep_summary(args, results)
     return 0
+
+
+def write_sweep_summary(args, results) -> None:
+    """profiles/sweep_mla_decode.md from a whole-grid sweep."""
+    lines = ["# Sweep: KV bandwidth against context length and head count", "",
+             f"Kernel source sha256 {kernel_source_hash()[:16]}..., MI355X (gfx950).  Command:",
+             "", "```", f"python3 bench.py --sweep --steps {args.steps} --warmup {args.warmup}", "```", "",
+             "One point = batch x heads x context, one query token, contiguous cache, seeded N(0,1) bf16 inputs "
+             f"drawn on the device.  Each point: clocks settled for {args.settle_s:g} s, {args.warmup} warmup steps, "
+             f"{args.steps} timed steps (wall clock, `us/call`), then {args.steps} more with HIP events around the "
+             "split kernel.  Points under 1 GiB of KV rotate over copies so every step streams from HBM.", "",
+             "| batch | heads | context | KV MB | us/call | GB/s (call) | split us | split GB/s | split % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in results:
+        lines.append(f"| {r['batch']} | {r['heads']} | {r['kv_len']} | {r['kv_bytes'] / 1e6:,.1f} | "
+                     f"{r['us_per_call']:.2f} | {r['GBps']:,.0f} | {r['split_us']:.2f} | {r['split_GBps']:,.0f} | "
+                     f"{100 * r['split_frac_of_8TBps']:.1f}% |")
+    os.makedirs(args.profiles_out, exist_ok=True)
+    with open(os.path.join(args.profiles_out, "sweep_mla_decode.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def mla_steps(args) -> int:

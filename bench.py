@@ -120,6 +120,7 @@ def sweep(args) -> int:
     ctx = mla.Context()
     ctx.set_option(mla.MLA_OPT_NUM_SPLITS, args.splits)
     ctx.set_option(mla.MLA_OPT_MIN_CHUNK, args.min_chunk)
+    ctx.set_option(mla.MLA_OPT_P_BF16, int(args.p_bf16))
     scale = 1.0 / 24.0
     results = []
     for B, s_q, H, L in points:
@@ -182,7 +183,8 @@ def write_sweep_summary(args, results) -> None:
     """profiles/sweep_mla_decode.md from a whole-grid sweep."""
     lines = ["# Sweep: KV bandwidth against context length and head count", "",
              f"Kernel source sha256 {kernel_source_hash()[:16]}..., MI355X (gfx950).  Command:",
-             "", "```", f"python3 bench.py --sweep --steps {args.steps} --warmup {args.warmup}", "```", "",
+             "", "```", f"python3 bench.py --sweep --steps {args.steps} --warmup {args.warmup}"
+             + (" --p-bf16" if args.p_bf16 else ""), "```", "",
              "One point = batch x heads x context, one query token, contiguous cache, seeded N(0,1) bf16 inputs "
              f"drawn on the device.  Each point: clocks settled for {args.settle_s:g} s, {args.warmup} warmup steps, "
              f"{args.steps} timed steps (wall clock, `us/call`), then {args.steps} more with HIP events around the "
@@ -641,6 +643,9 @@ def main() -> int:
     ap.add_argument("--step-shape", default="16,1,16", help="B,s_q,H of --mla-steps")
     ap.add_argument("--splits", type=int, default=0, help="key ranges per launch (0: library default)")
     ap.add_argument("--min-chunk", type=int, default=0, help="smallest key range (0: library default)")
+    ap.add_argument("--p-bf16", action="store_true",
+                    help="MLA_OPT_P_BF16: P as one bf16 value in the kernels whose row blocks share key steps "
+                         "(faster, each P term within 2^-9 of itself; off by default)")
     ap.add_argument("--collect-counters", default="",
                     help="comma-separated workloads: run the rocprofv3 counter passes of their split kernel "
                          "(each pass a child run) and write profiles/traffic_* and profiles/counters_*")
@@ -701,6 +706,7 @@ def main() -> int:
     ctx = mla.Context()
     ctx.set_option(mla.MLA_OPT_NUM_SPLITS, args.splits)
     ctx.set_option(mla.MLA_OPT_MIN_CHUNK, args.min_chunk)
+    ctx.set_option(mla.MLA_OPT_P_BF16, int(args.p_bf16))
     ctx.reserve(w.s_q, w.heads)
 
     def step(i):
@@ -764,7 +770,8 @@ def main() -> int:
                    "kv_len": w.seqlen if isinstance(w.seqlen, int) else list(w.seqlen),
                    "layout": "paged%d" % w.page_size if w.page_size else "contiguous",
                    "kv_bytes": kv_bytes, "cache_copies_rotated": len(copies), "warm": bool(args.warm),
-                   "splits": args.splits or "default", "min_chunk": args.min_chunk or "default"},
+                   "splits": args.splits or "default", "min_chunk": args.min_chunk or "default",
+                   "p_bf16": bool(args.p_bf16)},
         "roofline": {
             "bound": "hbm",
             "kernel": "mla_split_kernel",

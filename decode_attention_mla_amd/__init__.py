@@ -26,7 +26,7 @@ HEAD_DIM_V = 512
 KEY_BLOCK = 16
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
-MLA_OPT_NUM_SPLITS, MLA_OPT_MIN_CHUNK, MLA_OPT_KERNEL_TIMING = 1, 2, 3
+MLA_OPT_NUM_SPLITS, MLA_OPT_MIN_CHUNK, MLA_OPT_KERNEL_TIMING, MLA_OPT_P_BF16 = 1, 2, 3, 4
 
 
 class MlaError(RuntimeError):

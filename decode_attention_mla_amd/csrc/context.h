@@ -19,6 +19,7 @@ struct mla_ctx {
     int64_t opt_splits = 0;
     int64_t opt_min_chunk = mla::kDefaultMinChunk;
     bool timing = false;
+    bool p_bf16 = false;  // MLA_OPT_P_BF16
     // Split workspace: either the library's own (allocated on first use or
     // by mla_ctx_reserve, grown by allocating a larger one) or a caller's
     // buffer (mla_ctx_set_workspace).  A replaced buffer of the library's

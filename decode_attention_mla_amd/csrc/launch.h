@@ -32,9 +32,11 @@ size_t workspace_bytes(int splits, int n_rb);
 // Enqueue the split kernel(s) and, when some sequence is split across key
 // ranges, the combine kernel on `stream`, with the partials in `ws`
 // (workspace_bytes(splits, n_rb) bytes).  The arguments must already have
-// passed the host checks of mla_decode.  `ev` (may be NULL) gets its events
-// recorded.  On failure returns the HIP error and names the launch in *what.
-hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, void *ws, const void *q,
+// passed the host checks of mla_decode.  `p_bf16`: P enters the PV product
+// as one bf16 value in the kernels whose row blocks share key steps (see
+// MLA_OPT_P_BF16).  `ev` (may be NULL) gets its events recorded.  On failure
+// returns the HIP error and names the launch in *what.
+hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool p_bf16, void *ws, const void *q,
                          const void *kv_cache, const int32_t *block_table, const int32_t *seqlens, float scale,
                          float *out, float *lse, const mla_problem *p, LaunchEvents *ev, const char **what);
 

@@ -187,6 +187,10 @@ int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value) {
     case MLA_OPT_KERNEL_TIMING:
         ctx->timing = value != 0;
         return MLA_OK;
+    case MLA_OPT_P_BF16:
+        if (value != 0 && value != 1) return fail(ctx, MLA_ERR_INVALID_ARG, "MLA_OPT_P_BF16 takes 0 or 1");
+        ctx->p_bf16 = value != 0;
+        return MLA_OK;
     default:
         return fail(ctx, MLA_ERR_INVALID_ARG, "unknown option %d", option);
     }
@@ -333,8 +337,8 @@ int mla_decode(mla_ctx *ctx, const void *q, const void *kv_cache, const int32_t 
     mla::LaunchEvents evs;
     mla::LaunchEvents *ev = take_events(ctx, &evs);
     const char *what = "launch";
-    const hipError_t e = mla::launch_decode(ctx->stream, splits, min_chunk_of(ctx), ctx->ws, q, kv_cache,
-                                            block_table, seqlens, scale, out, lse, p, ev, &what);
+    const hipError_t e = mla::launch_decode(ctx->stream, splits, min_chunk_of(ctx), ctx->p_bf16, ctx->ws, q,
+                                            kv_cache, block_table, seqlens, scale, out, lse, p, ev, &what);
     keep_events(ctx, ev, e == hipSuccess);
     return e == hipSuccess ? MLA_OK : hip_fail(ctx, e, what);
 }

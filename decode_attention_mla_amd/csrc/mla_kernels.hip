@@ -689,7 +689,9 @@ __device__ inline void pair_scores(PairReads &rd, float (&sv)[8], float &mx, con
 // hi and lo halves (two MFMAs per tile), and V^T (A operand) joins one
 // transposing read of each block.  Within a group of four tiles the hi
 // MFMAs come before the lo ones, so no MFMA waits on the one before it.
-template <typename Side = NoSide>
+// kHiOnly (the caller's MLA_OPT_P_BF16): P enters as its bf16 hi half alone,
+// half the MFMAs, each P term rounded by at most 2^-9 of itself.
+template <bool kHiOnly = false, typename Side = NoSide>
 __device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8], Side side = Side{}) {
     bf16x8 phi, plo;
     float psum = 0.f;
@@ -699,7 +701,7 @@ __device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8
         psum += pr;
         const __bf16 hb = static_cast<__bf16>(pr);
         phi[i] = hb;
-        plo[i] = static_cast<__bf16>(pr - static_cast<float>(hb));
+        if constexpr (!kHiOnly) plo[i] = static_cast<__bf16>(pr - static_cast<float>(hb));
     }
     ws.l += psum;
     __builtin_amdgcn_sched_barrier(0);
@@ -708,7 +710,11 @@ __device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8
         const int ct = 4 * (m >> 3) + (m & 3);
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(rd.vr[2 * ct], rd.vr[2 * ct + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-        ws.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (m & 4) ? plo : phi, ws.acc[ct], 0, 0, 0);
+        // With kHiOnly the lo MFMAs drop out; the operand reads and the
+        // loads that go with them keep their places in the stream.
+        if (!(kHiOnly && (m & 4)))
+            ws.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (!kHiOnly && (m & 4)) ? plo : phi, ws.acc[ct],
+                                                                 0, 0, 0);
         rd.read(kPairK + kAhead + m);
         side(kPairK + m);
         __builtin_amdgcn_sched_barrier(0);
@@ -825,7 +831,7 @@ __device__ inline void write_rows(const Params &p, const WaveState &ws, int b, i
 //              of each step's loads, and each wave writes its rows itself.
 enum SplitMode { kOneBlock = 0, kTwoGroups = 1, kOneGroup = 2 };
 
-template <int kMode>
+template <int kMode, bool kHiOnly>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_split_kernel(Params p) {
     constexpr bool kShared = kMode != kOneBlock;
@@ -1058,7 +1064,7 @@ void mla_split_kernel(Params p) {
                     float sv[8], mx;
                     pair_scores(rd, sv, mx, qf, kbp, key_end, p.scale_log2, lane, side);
                     if (__any(mx > ws.m + kMaxLag)) rescale(ws, mx);  // rare
-                    pair_pv(rd, ws, sv, side);
+                    pair_pv<kHiOnly>(rd, ws, sv, side);
                 };
                 auto step = [&](auto slot_idx, int i) __attribute__((always_inline)) {
                     constexpr int P = decltype(slot_idx)::value;
@@ -1243,7 +1249,7 @@ size_t workspace_bytes(int splits, int n_rb) {
     return rows * (kDv + 1) * sizeof(float) + 256;
 }
 
-hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, void *ws, const void *q,
+hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool p_bf16, void *ws, const void *q,
                          const void *kv_cache, const int32_t *block_table, const int32_t *seqlens, float scale,
                          float *out, float *lse, const mla_problem *p, LaunchEvents *ev, const char **what) {
     const int n_rb = p->s_q * p->num_heads / 16;
@@ -1297,7 +1303,11 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, void
     hipError_t e = hipSuccess;
     if (full > 0) {
         prm.y0 = 0;
-        hipLaunchKernelGGL(mla_split_kernel<kOneGroup>, dim3(grid_x, full), dim3(kThreads), 0, stream, prm);
+        if (p_bf16)
+            hipLaunchKernelGGL((mla_split_kernel<kOneGroup, true>), dim3(grid_x, full), dim3(kThreads), 0, stream, prm);
+        else
+            hipLaunchKernelGGL((mla_split_kernel<kOneGroup, false>), dim3(grid_x, full), dim3(kThreads), 0, stream,
+                               prm);
         e = hipGetLastError();
         if (e != hipSuccess) {
             *what = "mla_split_kernel launch";
@@ -1307,9 +1317,12 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, void
     if (rem == 1 || rem == 2) {
         prm.y0 = n_rb / kWaves;
         if (rem == 1)
-            hipLaunchKernelGGL(mla_split_kernel<kOneBlock>, dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
+            hipLaunchKernelGGL((mla_split_kernel<kOneBlock, false>), dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
+        else if (p_bf16)
+            hipLaunchKernelGGL((mla_split_kernel<kTwoGroups, true>), dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
         else
-            hipLaunchKernelGGL(mla_split_kernel<kTwoGroups>, dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
+            hipLaunchKernelGGL((mla_split_kernel<kTwoGroups, false>), dim3(grid_x, 1), dim3(kThreads), 0, stream,
+                               prm);
         e = hipGetLastError();
         if (e != hipSuccess) {
             *what = "mla_split_kernel launch";

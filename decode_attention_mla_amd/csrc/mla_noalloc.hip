@@ -106,8 +106,8 @@ int mla_decode_noalloc(void *stream, const void *q, const void *kv_cache, const 
                     kScratchBytes);
 
     const char *what = "launch";
-    e = mla::launch_decode((hipStream_t)stream, splits, mla::kDefaultMinChunk, ds.ptr, q, kv_cache, block_table,
-                           seqlens, scale, out, lse, p, nullptr, &what);
+    e = mla::launch_decode((hipStream_t)stream, splits, mla::kDefaultMinChunk, false, ds.ptr, q, kv_cache,
+                           block_table, seqlens, scale, out, lse, p, nullptr, &what);
     return e == hipSuccess ? MLA_OK : hip_fail(nullptr, e, what);
 }
 

@@ -150,11 +150,27 @@ int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads);
  *                      64, rounded up to MLA_KEY_BLOCK); 0 restores it.
  *  MLA_OPT_KERNEL_TIMING  1: bracket every kernel launch with HIP events on
  *                      the context's stream (see mla_ctx_kernel_times); 0: off.
+ *
+ * A precision knob (default off; the only option that changes results):
+ *  MLA_OPT_P_BF16      1: where several 16-row blocks of a sequence share
+ *                      each key step (s_q * num_heads >= 32; a last lone
+ *                      block of 16 rows is not affected), the softmax
+ *                      weights P enter P V as one bf16 value each instead of
+ *                      a bf16 high part plus a bf16 remainder, which halves
+ *                      that product's MFMA work.  Each weight is then off by
+ *                      at most 2^-9 of itself, so every O element moves by
+ *                      at most 2^-9 * max_j |V[j][c]| (plus fp32 rounding)
+ *                      from the default result (the sum and the LSE keep
+ *                      fp32 weights).  On N(0,1) inputs that
+ *                      is an O RMSE of about 1e-5 at 64K keys and 1e-4 at 512.
+ *                      With 16 rows (one block) it changes nothing: there
+ *                      both parts cost one MFMA.  0: the default.
  */
 typedef enum {
     MLA_OPT_NUM_SPLITS = 1,
     MLA_OPT_MIN_CHUNK = 2,
-    MLA_OPT_KERNEL_TIMING = 3
+    MLA_OPT_KERNEL_TIMING = 3,
+    MLA_OPT_P_BF16 = 4
 } mla_option;
 int mla_ctx_set_option(mla_ctx *ctx, int option, int64_t value);
 

@@ -39,8 +39,10 @@ def steps_asm(tmp_path_factory):
 
 
 # Every instance of the split kernel: one row block per workgroup, two key
-# groups, one key group.
-SPLIT_KERNELS = tuple(f"_ZN3mla16mla_split_kernelILi{m}EEEvNS_6ParamsE" for m in range(3))
+# groups, one key group; the shared-step ones also with P as one bf16
+# (MLA_OPT_P_BF16).
+SPLIT_KERNELS = tuple(f"_ZN3mla16mla_split_kernelILi{m}ELb{h}EEEvNS_6ParamsE"
+                      for m, h in ((0, 0), (1, 0), (1, 1), (2, 0), (2, 1)))
 
 
 def kernel_body(asm, name):

@@ -35,6 +35,24 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), f"{name} declared in mla_decode.h but not exported"
 
 
+def declared_constants():
+    """Every `MLA_NAME = value` of the header's enums and defines."""
+    text = open(mla.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    found = dict(re.findall(r"\b(MLA_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
+    found.update(re.findall(r"#define\s+(MLA_[A-Z0-9_]+)\s+(-?\d+)\b", text))
+    return {k: int(v) for k, v in found.items()}
+
+
+def test_binding_constants_match_the_header():
+    """The binding's status codes and option ids are the header's values."""
+    consts = declared_constants()
+    for name in ("MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_WORKSPACE", "MLA_ERR_HIP",
+                 "MLA_OPT_NUM_SPLITS", "MLA_OPT_MIN_CHUNK", "MLA_OPT_KERNEL_TIMING", "MLA_OPT_P_BF16"):
+        assert name in consts, f"{name} missing from mla_decode.h"
+        assert getattr(mla, name) == consts[name], name
+
+
 def test_version(lib):
     assert "gfx950" in mla.version()
 

@@ -645,7 +645,7 @@ def main() -> int:
     ap.add_argument("--min-chunk", type=int, default=0, help="smallest key range (0: library default)")
     ap.add_argument("--p-bf16", action="store_true",
                     help="MLA_OPT_P_BF16: P as one bf16 value in the kernels whose row blocks share key steps "
-                         "(faster, each P term within 2^-9 of itself; off by default)")
+                         "(faster, each P term within 2^-8 of itself; off by default)")
     ap.add_argument("--collect-counters", default="",
                     help="comma-separated workloads: run the rocprofv3 counter passes of their split kernel "
                          "(each pass a child run) and write profiles/traffic_* and profiles/counters_*")

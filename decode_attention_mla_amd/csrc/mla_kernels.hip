@@ -690,7 +690,8 @@ __device__ inline void pair_scores(PairReads &rd, float (&sv)[8], float &mx, con
 // transposing read of each block.  Within a group of four tiles the hi
 // MFMAs come before the lo ones, so no MFMA waits on the one before it.
 // kHiOnly (the caller's MLA_OPT_P_BF16): P enters as its bf16 hi half alone,
-// half the MFMAs, each P term rounded by at most 2^-9 of itself.
+// half the MFMAs, each P term rounded by at most 2^-8 of itself (bf16 keeps 8
+// significant bits).
 template <bool kHiOnly = false, typename Side = NoSide>
 __device__ inline void pair_pv(PairReads &rd, WaveState &ws, const float (&sv)[8], Side side = Side{}) {
     bf16x8 phi, plo;

@@ -158,8 +158,9 @@ int mla_ctx_reserve(mla_ctx *ctx, int32_t s_q, int32_t num_heads);
  *                      weights P enter P V as one bf16 value each instead of
  *                      a bf16 high part plus a bf16 remainder, which halves
  *                      that product's MFMA work.  Each weight is then off by
- *                      at most 2^-9 of itself, so every O element moves by
- *                      at most 2^-9 * max_j |V[j][c]| (plus fp32 rounding)
+ *                      at most 2^-8 of itself (bf16 keeps 8 significant
+ *                      bits), so every O element moves by at most
+ *                      2^-8 * max_j |V[j][c]| (plus fp32 rounding)
  *                      from the default result (the sum and the LSE keep
  *                      fp32 weights).  On N(0,1) inputs that
  *                      is an O RMSE of about 1e-5 at 64K keys and 1e-4 at 512.

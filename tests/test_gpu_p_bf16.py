@@ -2,8 +2,8 @@
 blocks share key steps.
 
 Bound (derived from the arithmetic): each weight p_j is rounded to bf16, so
-p_j (1 + d_j) with |d_j| <= 2^-9, while the sum l and the LSE keep the fp32
-weights.  Then O_c moves by sum_j p_j d_j v_jc / l, at most 2^-9 max_j |v_jc|
+p_j (1 + d_j) with |d_j| <= 2^-8 (8 significant bits, rounded to nearest), while the sum l and the LSE keep the fp32
+weights.  Then O_c moves by sum_j p_j d_j v_jc / l, at most 2^-8 max_j |v_jc|
 over the sequence's keys; the key-group merge and the split combine are
 weighted averages and keep that bound.  The tests check every element
 against the fp64 oracle within that bound (plus the default path's 1e-5),
@@ -21,7 +21,7 @@ from gpu_util import LSE_MAXABS_MAX, compare, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
-ROUNDING = 2.0 ** -9
+ROUNDING = 2.0 ** -8  # unit roundoff of bf16
 SLACK = 1e-5  # the default path's own error, far above its measured 1e-7
 
 
@@ -120,5 +120,37 @@ def test_option_values(mla):
         with pytest.raises(mla.MlaError):
             ctx.set_option(mla.MLA_OPT_P_BF16, 2)
         ctx.set_option(mla.MLA_OPT_P_BF16, 0)
+    finally:
+        ctx.close()
+
+
+N_FUZZ = 60
+
+
+def test_random_shapes_within_the_bound(mla):
+    """The seeded random shapes of the default fuzz (batch, lengths, tokens,
+    heads, pages, forced splits, peaked queries), with the option on: every
+    element within the rounding bound, the LSE within the default bar."""
+    from test_gpu_fuzz import draw_case
+
+    ctx = mla.Context()
+    ctx.set_option(mla.MLA_OPT_P_BF16, 1)
+    try:
+        for i in range(N_FUZZ):
+            c = draw_case(i)
+            print(f"[p-bf16 fuzz {i}] {c}", flush=True)
+            sys.stdout.flush()
+            inp = wl.small("fz", c["B"], c["s_q"], c["H"], c["lens"], page_size=c["page"], seed=c["seed"])
+            if c["q_scale"] != 1.0:
+                inp.q[:] = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(inp.q) * np.float32(c["q_scale"]))
+            ctx.set_option(mla.MLA_OPT_NUM_SPLITS, c["splits"])
+            ctx.set_option(mla.MLA_OPT_MIN_CHUNK, c["min_chunk"])
+            o, l = run_gpu(ctx, inp, host_lens=c["host_lens"])
+            ro, rl = oracle.mla_decode(inp.q, inp.kv, inp.block_table, inp.seqlens, inp.scale)
+            bound = ROUNDING * v_max(inp)[:, None, None, :] + SLACK
+            assert np.isfinite(o).all() and np.isfinite(l).all(), f"case {i}"
+            excess = np.abs(o - ro) - bound
+            assert excess.max() <= 0, f"case {i} {c}: {int((excess > 0).sum())} elements past the bound"
+            assert np.abs(l - rl).max() <= LSE_MAXABS_MAX, f"case {i} {c}: LSE"
     finally:
         ctx.close()

@@ -114,9 +114,9 @@ def sweep(args) -> int:
     points = [(b, 1, 16, L) for b in (16, 32) for L in (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536)]
     points += [(16, 1, h, 65536) for h in (32, 64, 128)]
     if args.sweep_points:
-        keep = {tuple(int(x) for x in p.split("x")) for p in args.sweep_points.split(",")}
-        points = [pt for pt in points if (pt[0], pt[2], pt[3]) in keep] or \
-                 [(b, 1, h, L) for b, h, L in sorted(keep)]
+        # exactly the requested BxHxL points, in the order given
+        points = [(b, 1, h, L) for b, h, L in
+                  (tuple(int(x) for x in pt.split("x")) for pt in args.sweep_points.split(","))]
     ctx = mla.Context()
     ctx.set_option(mla.MLA_OPT_NUM_SPLITS, args.splits)
     ctx.set_option(mla.MLA_OPT_MIN_CHUNK, args.min_chunk)

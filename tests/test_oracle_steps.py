@@ -6,7 +6,6 @@ one (keys and values up-projected per head).  CPU only."""
 from fractions import Fraction
 
 import numpy as np
-import pytest
 
 import workloads as wl
 from oracle import steps

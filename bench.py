@@ -368,6 +368,9 @@ def mla_steps(args) -> int:
 
 SQ_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
                "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+# A second pass of eight more (at most eight SQ counters fit in one pass).
+SQ_COUNTERS_2 = ("SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                 "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_LDS_ADDR_CONFLICT")
 SIMDS = 1024  # 256 CUs x 4 SIMDs
 # Raw L2-to-memory read requests, all, 32-byte, 128-byte ("bubble") and
 # those sent on to DRAM: FETCH_SIZE is computed from the first three.
@@ -450,6 +453,7 @@ def collect_counters(args) -> int:
     # one kind): the size that FETCH_SIZE's expression should have used.
     copy_req = cr.get("TCC_EA0_RDREQ_sum", 0.0)
     req_size = copy_bytes / copy_req if copy_req else None
+    counter_recs = []
     for name in args.collect_counters.split(","):
         import workloads as wl
 
@@ -460,10 +464,12 @@ def collect_counters(args) -> int:
         rw, cmd_w = run(["WRITE_SIZE"], wargs)
         rs, cmd_s = run(list(SQ_COUNTERS), wargs)
         rr, cmd_r = run(list(TCC_READ_REQUESTS), wargs)
+        rs2, cmd_s2 = run(list(SQ_COUNTERS_2), wargs)
         ks, f = _kernel_entry(rf, "mla_split_kernel")
         _, rq = _kernel_entry(rr, "mla_split_kernel")
         _, wv = _kernel_entry(rw, "mla_split_kernel")
         _, sq = _kernel_entry(rs, "mla_split_kernel")
+        _, sq2 = _kernel_entry(rs2, "mla_split_kernel")
         kc, fc = _kernel_entry(rf, "mla_combine_kernel")
         _, wc = _kernel_entry(rw, "mla_combine_kernel")
         fetch_b = int(round(f["FETCH_SIZE"] * 1024 * fetch_factor))
@@ -499,14 +505,16 @@ def collect_counters(args) -> int:
         crec = {"kernel": "mla_split_kernel", "workload": name, "kernel_source_sha256": sha, "revision": rev,
                 "counters_per_dispatch": sq, "mfma_busy_pct": mfma_busy,
                 "mfma_busy_definition": "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8)",
-                "command": cmd_s}
+                "command": cmd_s, "counters_per_dispatch_2": sq2, "command_2": cmd_s2,
+                "derived": derived_counters(w, {**sq2, **sq}, mfma_busy)}
+        counter_recs.append(crec)
         with open(os.path.join(prof, f"counters_mla_split_{name}.json"), "w") as fh:
             json.dump(crec, fh, indent=1)
             fh.write("\n")
         lines = [f"# HBM traffic: mla_split_kernel, {name}", "",
                  f"Source revision {rev} (kernel source sha256 {sha[:16]}...). Counters in their own runs "
                  "(one counter group per run), written by `bench.py --collect-counters`:", "", "```",
-                 *cmds, cmd_s, "```", "",
+                 *cmds, "```", "",
                  f"Calibration: a plain 1 GiB device copy (`bench.py --calibrate-copy`) reads FETCH_SIZE = "
                  f"{cf['FETCH_SIZE']:,.1f} KiB and WRITE_SIZE = {cw['WRITE_SIZE']:,.1f} KiB per dispatch for "
                  f"1,048,576 KiB moved each way: factors {fetch_factor:.4f} (fetch) and {write_factor:.4f} (write).",
@@ -529,8 +537,9 @@ def collect_counters(args) -> int:
                       f"any other. At {req_size:.2f} B per request the split kernel's requests come to "
                       f"{rr_['request_bytes_per_launch']:,} B per launch, "
                       f"{rr_['request_bytes_over_algorithmic']:.4f} of the algorithmic bytes.", ""]
-        lines += ["SQ counters of the split kernel, mean per dispatch:", "", "| counter | value |", "|---|---|"]
-        lines += [f"| {c} | {v:,.0f} |" for c, v in sorted(sq.items())]
+        lines += ["SQ counters of the split kernel, mean per dispatch (two passes):", "", "```", cmd_s, cmd_s2,
+                  "```", "", "| counter | value |", "|---|---|"]
+        lines += [f"| {c} | {v:,.0f} |" for c, v in sorted({**sq2, **sq}.items())]
         if mfma_busy is not None:
             lines += ["", f"MFMA busy: {mfma_busy:.2f}% of SIMD time "
                       "(SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8))."]
@@ -539,7 +548,86 @@ def collect_counters(args) -> int:
         print(json.dumps({"mode": "collect-counters", "workload": name, "fetch_over_algorithmic":
                           round(fetch_b / kv_bytes, 4), "write_bytes": write_b, "mfma_busy_pct":
                           None if mfma_busy is None else round(mfma_busy, 2)}), flush=True)
+    write_counter_summary(args, counter_recs, rev, sha)
     return 0
+
+
+def derived_counters(w, c, mfma_busy):
+    """Per-unit figures from one workload's SQ counters (means per dispatch).
+    A block is 16 keys of one sequence; a row block is 16 query rows (one
+    token, 16 heads), so every block is computed once per row block.  SQ
+    wave-cycle counters share one unit, so their ratios are fractions of the
+    waves' lifetime."""
+    import workloads as wl
+
+    blocks = float(wl.draw_seqlens(w).astype("int64").sum()) / 16
+    n_rb = w.s_q * w.heads // 16
+    wave = c.get("SQ_WAVE_CYCLES", 0.0)
+
+    def ratio(a, b, scale=1.0):
+        return scale * a / b if b else None
+
+    return {
+        "blocks_of_16_keys": blocks, "row_blocks": n_rb,
+        "mfma_per_block_per_row_block": ratio(c.get("SQ_INSTS_MFMA", 0.0), blocks * n_rb),
+        "lds_insts_per_block_per_row_block": ratio(c.get("SQ_INSTS_LDS", 0.0), blocks * n_rb),
+        "valu_insts_per_block_per_row_block": ratio(c.get("SQ_INSTS_VALU", 0.0), blocks * n_rb),
+        "mfma_busy_cycles_per_mfma": ratio(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), c.get("SQ_INSTS_MFMA", 0.0)),
+        "lds_bank_conflict_cycles_per_block": ratio(c.get("SQ_LDS_BANK_CONFLICT", 0.0), blocks),
+        "mfma_busy_pct": mfma_busy,
+        "wait_any_pct_of_wave_cycles": ratio(c.get("SQ_WAIT_ANY", 0.0), wave, 100.0),
+        "wait_inst_any_pct_of_wave_cycles": ratio(c.get("SQ_WAIT_INST_ANY", 0.0), wave, 100.0),
+        "wait_inst_lds_pct_of_wave_cycles": ratio(c.get("SQ_WAIT_INST_LDS", 0.0), wave, 100.0),
+        "active_lds_pct_of_wave_cycles": ratio(c.get("SQ_ACTIVE_INST_LDS", 0.0), wave, 100.0),
+        "kernel_us_from_grbm_at_2_4_ghz": ratio(c.get("GRBM_GUI_ACTIVE", 0.0), 8 * 2400.0),
+    }
+
+
+DERIVED_ROWS = (
+    ("mfma_per_block_per_row_block", "MFMA instructions per 16-key block per row block", "{:.2f}"),
+    ("lds_insts_per_block_per_row_block", "LDS instructions per block per row block", "{:.2f}"),
+    ("valu_insts_per_block_per_row_block", "VALU instructions per block per row block", "{:.1f}"),
+    ("mfma_busy_cycles_per_mfma", "MFMA busy cycles per MFMA", "{:.2f}"),
+    ("lds_bank_conflict_cycles_per_block", "LDS bank-conflict cycles per block", "{:.2f}"),
+    ("mfma_busy_pct", "MFMA busy, % of SIMD time", "{:.2f}"),
+    ("wait_any_pct_of_wave_cycles", "waves waiting on counters (SQ_WAIT_ANY), % of wave cycles", "{:.2f}"),
+    ("wait_inst_any_pct_of_wave_cycles", "waves waiting to issue (SQ_WAIT_INST_ANY), % of wave cycles", "{:.2f}"),
+    ("wait_inst_lds_pct_of_wave_cycles", "waves waiting to issue LDS (SQ_WAIT_INST_LDS), % of wave cycles",
+     "{:.2f}"),
+    ("active_lds_pct_of_wave_cycles", "LDS instructions active (SQ_ACTIVE_INST_LDS), % of wave cycles", "{:.2f}"),
+    ("kernel_us_from_grbm_at_2_4_ghz", "kernel time from GRBM_GUI_ACTIVE / 8 at 2.4 GHz, us", "{:.2f}"),
+)
+
+
+def write_counter_summary(args, recs, rev, sha) -> None:
+    """profiles/counters_mla_split.md: the SQ counters of every workload of
+    one --collect-counters run side by side, with per-unit figures."""
+    if not recs:
+        return
+    names = [r["workload"] for r in recs]
+    counters = sorted({c for r in recs for c in (*r["counters_per_dispatch"], *r["counters_per_dispatch_2"])})
+    lines = ["# SQ counters of mla_split_kernel, by workload", "",
+             f"Source revision {rev} (kernel source sha256 {sha[:16]}...), MI355X (gfx950), ROCm 7.2. Written by "
+             "`bench.py --collect-counters`; two SQ passes per workload, each in a run of its own:", "", "```"]
+    for r in recs:
+        lines += [r["command"], r["command_2"]]
+    lines += ["```", "", "Mean per dispatch. SQ wave and busy counters tick once per 4 cycles; GRBM_GUI_ACTIVE is "
+              "summed over the 8 XCDs.", "", "| counter | " + " | ".join(names) + " |",
+              "|---|" + "---|" * len(names)]
+    for c in counters:
+        vals = []
+        for r in recs:
+            v = r["counters_per_dispatch"].get(c, r["counters_per_dispatch_2"].get(c))
+            vals.append("" if v is None else f"{v:,.0f}")
+        lines.append(f"| {c} | " + " | ".join(vals) + " |")
+    lines += ["", "Derived (a block is 16 keys; a row block is 16 query rows, so each block is computed once per "
+              "row block):", "", "| quantity | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for key, label, fmt in DERIVED_ROWS:
+        vals = [r["derived"].get(key) for r in recs]
+        lines.append(f"| {label} | " + " | ".join("" if v is None else fmt.format(v) for v in vals) + " |")
+    os.makedirs(args.profiles_out, exist_ok=True)
+    with open(os.path.join(args.profiles_out, "counters_mla_split.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def trace_summary(args) -> int:

@@ -64,7 +64,7 @@ def test_counter_summary_from_raw_output(tmp_path):
     copy, split = "__amd_rocclr_copyBuffer", "void mla::mla_split_kernel<0>(mla::Params)"
     gib_kib = 1 << 20
     d = tmp_path / "raw"
-    # the passes in the order bench.py runs them: the copy's three, then the workload's four
+    # the passes in the order bench.py runs them: the copy's three, then the workload's five
     _counter_csv(d / "pass1", [(1, copy, "FETCH_SIZE", gib_kib / 2)])
     _counter_csv(d / "pass2", [(1, copy, "WRITE_SIZE", gib_kib)])
     _counter_csv(d / "pass3", [(1, copy, "TCC_EA0_RDREQ_sum", (1 << 30) // 128),
@@ -74,9 +74,12 @@ def test_counter_summary_from_raw_output(tmp_path):
     # two dispatches of the split kernel: the summary takes their mean
     _counter_csv(d / "pass4", [(1, split, "FETCH_SIZE", kv / 2 / 1024), (2, split, "FETCH_SIZE", kv / 2 / 1024)])
     _counter_csv(d / "pass5", [(1, split, "WRITE_SIZE", 256.0)])
-    _counter_csv(d / "pass6", [(1, split, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0), (1, split, "GRBM_GUI_ACTIVE", 80.0)])
+    # 512 keys = 32 blocks of 16 keys, one row block: 50 MFMAs of 16 busy cycles per block
+    _counter_csv(d / "pass6", [(1, split, "SQ_INSTS_MFMA", 1600.0), (1, split, "SQ_VALU_MFMA_BUSY_CYCLES", 25600.0),
+                               (1, split, "SQ_WAVE_CYCLES", 10000.0), (1, split, "GRBM_GUI_ACTIVE", 8000.0)])
     _counter_csv(d / "pass7", [(1, split, "TCC_EA0_RDREQ_sum", kv // 128 + 10), (1, split, "TCC_EA0_RDREQ_32B_sum", 0),
                                (1, split, "TCC_BUBBLE_sum", 0), (1, split, "TCC_EA0_RDREQ_DRAM_sum", kv // 128)])
+    _counter_csv(d / "pass8", [(1, split, "SQ_WAIT_ANY", 2500.0), (1, split, "SQ_INSTS_VALU", 6400.0)])
     prof = tmp_path / "prof"
     r = run_bench("--collect-counters", "mla_bs1_ctx512", "--counters-reuse", "--counters-dir", str(d),
                   "--profiles-out", str(prof))
@@ -88,9 +91,16 @@ def test_counter_summary_from_raw_output(tmp_path):
     assert rq["bytes_per_request_from_copy"] == 128.0
     assert rq["request_bytes_per_launch"] == kv + 10 * 128
     counters = json.loads((prof / "counters_mla_split_mla_bs1_ctx512.json").read_text())
-    assert counters["mfma_busy_pct"] == 100.0 * 1024 / (1024 * 80 / 8)
+    assert counters["mfma_busy_pct"] == 100.0 * 25600 / (1024 * 8000 / 8)
+    der = counters["derived"]
+    assert der["mfma_per_block_per_row_block"] == 50.0 and der["mfma_busy_cycles_per_mfma"] == 16.0
+    assert der["valu_insts_per_block_per_row_block"] == 200.0 and der["wait_any_pct_of_wave_cycles"] == 25.0
     md = (prof / "traffic_mla_split_mla_bs1_ctx512.md").read_text()
-    assert "128.00 B per request" in md and "TCC_BUBBLE_sum" in md
+    assert "128.00 B per request" in md and "TCC_BUBBLE_sum" in md and "SQ_WAIT_ANY" in md
+    summary = (prof / "counters_mla_split.md").read_text()
+    assert "| MFMA instructions per 16-key block per row block | 50.00 |" in summary
+    assert "| waves waiting on counters (SQ_WAIT_ANY), % of wave cycles | 25.00 |" in summary
+    assert "| SQ_WAIT_ANY | 2,500 |" in summary
 
 
 def test_trace_summary_from_raw_output(tmp_path):

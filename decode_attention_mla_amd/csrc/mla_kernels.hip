@@ -110,25 +110,44 @@ struct Params {
     int32_t max_pages;
     int32_t n_rb;      // row blocks: s_q * heads / 16
     int32_t splits;    // key ranges (gridDim.x of the split kernel when sized blind)
-    int32_t y0;        // row-block group of blockIdx.y == 0
+    int32_t y0;        // first row-block group of the launch
+    int32_t n_groups;  // row-block groups in the launch (workgroups: key ranges x n_groups)
     float scale_log2;  // scale * log2(e)
 };
 
 // ---------------------------------------------------------------- wave helpers
 
-__device__ inline int64_t wave_sum_i64(int64_t v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-    return v;
+// Lane moves within the wave (DPP): row_shr:n takes lane i - n of the same
+// 16-lane row, row_bcast:15 lane 15 of the row before, row_bcast:31 lane 31.
+// Lanes whose row (row_mask) or 4-lane bank (bank_mask) is off, or whose
+// source lies outside the row, read 0.  No LDS round trip is involved.
+template <int kCtrl, int kRowMask, int kBankMask>
+__device__ inline uint32_t dpp_move(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, kBankMask, true);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr3 = 0x113, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes: sums of up to four lanes back
+// within a row, then of 4 and 8 back (the lanes that have them), then the
+// row totals carried into the rows after them.
+__device__ inline uint32_t wave_incl_scan_u32(uint32_t x) {
+    uint32_t s = x + dpp_move<kRowShr1, 0xf, 0xf>(x);
+    s += dpp_move<kRowShr2, 0xf, 0xf>(x);
+    s += dpp_move<kRowShr3, 0xf, 0xf>(x);
+    s += dpp_move<kRowShr4, 0xf, 0xe>(s);
+    s += dpp_move<kRowShr8, 0xf, 0xc>(s);
+    s += dpp_move<kRowBcast15, 0xa, 0xf>(s);
+    s += dpp_move<kRowBcast31, 0xc, 0xf>(s);
+    return s;
 }
 
-__device__ inline int64_t wave_incl_scan_i64(int64_t v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int64_t t = __shfl_up(v, d);
-        if (lane >= d) v += t;
-    }
-    return v;
+// Inclusive prefix sum of padded lengths (each below 2^32) over the lanes,
+// as two 16-bit halves whose 64-lane sums fit in 32 bits.
+__device__ inline int64_t wave_incl_scan_len(int64_t v) {
+    const uint32_t hi = wave_incl_scan_u32((uint32_t)((uint64_t)v >> 16));
+    const uint32_t lo = wave_incl_scan_u32((uint32_t)v & 0xffffu);
+    return ((int64_t)hi << 16) + lo;
 }
 
 // Values that are the same in every lane, moved to scalar registers so that
@@ -146,36 +165,49 @@ __device__ inline int64_t lane_value(int64_t v, int j) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Workgroup id -> key range g and row-block group grp.  The n_groups
+// workgroups of one key range read the same keys.  Ids go round-robin over
+// the 8 XCDs, so ids 8 apart share an XCD (and its L2) and are dispatched
+// close together: each block of 8 x n_groups ids holds 8 ranges x n_groups
+// groups, range-minor, so that the groups of a range read its keys in step
+// and all but the first read them from that L2.  Ranges past the last
+// multiple of 8 follow in plain order.  One group: g = id.
+__device__ inline void range_and_group(int id, int n_groups, int ranges, int &g, int &grp) {
+    const int full8 = ranges / 8 * 8;
+    if (id < full8 * n_groups) {
+        const int w = id % (8 * n_groups);
+        g = id / (8 * n_groups) * 8 + w % 8;
+        grp = w / 8;
+    } else {
+        const int t = id - full8 * n_groups, rem = ranges - full8;
+        g = full8 + t % rem;
+        grp = t / rem;
+    }
+}
+
 __device__ inline int32_t seq_len(const Params &p, int b) {
     return clamp_len(p.seqlens[b], p.capacity);
 }
 
-// Total padded keys over all sequences (every lane gets the sum).
-__device__ inline int64_t plan_total(const Params &p, int lane) {
-    int64_t total = 0;
-    for (int b0 = 0; b0 < p.batch; b0 += 64) {
-        const int b = b0 + lane;
-        total += wave_sum_i64(b < p.batch ? padded_len(seq_len(p, b)) : 0);
-    }
-    return uniform(total);
-}
-
 // Where sequence b lies on the line of padded keys: its start, its padded
 // length, and the total over all sequences (every lane gets all three).
-// One length load per lane per 64 sequences, all issued before any sum.
+// One length load per lane per 64 sequences and one prefix sum of them.
 __device__ inline void line_position(const Params &p, int b, int lane, int64_t &total,
                                      int64_t &start, int64_t &len) {
     int64_t t = 0, s = 0, l = 0;
     for (int b0 = 0; b0 < p.batch; b0 += 64) {
         const int bl = b0 + lane;
         const int64_t lpl = bl < p.batch ? padded_len(seq_len(p, bl)) : 0;
-        t += lpl;
-        s += bl < b ? lpl : 0;
-        l += bl == b ? lpl : 0;
+        const int64_t incl = wave_incl_scan_len(lpl);
+        if (b >= b0 && b < b0 + 64) {
+            l = lane_value(lpl, b - b0);
+            s = t + lane_value(incl, b - b0) - l;
+        }
+        t += lane_value(incl, 63);
     }
-    total = uniform(wave_sum_i64(t));
-    start = uniform(wave_sum_i64(s));
-    len = uniform(wave_sum_i64(l));
+    total = uniform(t);
+    start = uniform(s);
+    len = uniform(l);
 }
 
 __device__ inline uint16_t bf16_bits(float x) {
@@ -735,14 +767,38 @@ struct MergeArea {
     __device__ float *row(int w, int head) const {
         return reinterpret_cast<float *>(w < 2 ? stage0 : stage1) + ((w & 1) * 16 + head) * kMergePitch;
     }
+    __device__ float *m_at(int w, int head) const { return m + w * 16 + head; }
+    __device__ float *l_at(int w, int head) const { return l + w * 16 + head; }
+};
+
+// One row block per workgroup: each wave's O rows and stats go into its own
+// two ring blocks, rows 0-7 into its stage-0 block with the stats after
+// them and rows 8-15 into its stage-1 block, shifted by 32 floats so that
+// the rows of heads h and h + 8 start on different banks.  No other wave
+// touches those blocks, so a wave writes its rows as soon as its own last
+// block is done.
+constexpr int kMergeHiShift = 32;
+static_assert(8 * kMergePitch * 4 + 32 * 4 <= kBlockBytes, "rows 0-7 and the stats fit in a block");
+static_assert((kMergeHiShift + 8 * kMergePitch) * 4 <= kBlockBytes, "rows 8-15 fit in a block");
+struct WaveMergeArea {
+    char *stage0, *stage1;
+    __device__ float *row(int w, int head) const {
+        return head < 8 ? reinterpret_cast<float *>(stage0 + w * kBlockBytes) + head * kMergePitch
+                        : reinterpret_cast<float *>(stage1 + w * kBlockBytes) + kMergeHiShift +
+                              (head - 8) * kMergePitch;
+    }
+    __device__ float *m_at(int w, int head) const {
+        return reinterpret_cast<float *>(stage0 + w * kBlockBytes) + 8 * kMergePitch + head;
+    }
+    __device__ float *l_at(int w, int head) const { return m_at(w, head) + 16; }
 };
 
 // Rows of row block rb0 + rbl from the NKG waves that computed them (waves
 // rbl + nrb kg): the LSE-weighted sum of their O rows, normalized, written
 // as the final rows (whole) or as the segment's part.  Every LDS read is
 // issued before the first is used.  256 threads: 16 heads x 16 quads.
-template <int NKG>
-__device__ inline void merge_waves(const Params &p, const MergeArea &ma, int b, int rb0, int rbl, int nrb,
+template <int NKG, typename Area>
+__device__ inline void merge_waves(const Params &p, const Area &ma, int b, int rb0, int rbl, int nrb,
                                    bool whole, int slot) {
     const int head = threadIdx.x >> 4;
     const int cq = threadIdx.x & 15;
@@ -751,8 +807,8 @@ __device__ inline void merge_waves(const Params &p, const MergeArea &ma, int b, 
 #pragma unroll
     for (int kg = 0; kg < NKG; ++kg) {
         const int w = rbl + nrb * kg;
-        mw[kg] = ma.m[w * 16 + head];
-        lw[kg] = ma.l[w * 16 + head];
+        mw[kg] = *ma.m_at(w, head);
+        lw[kg] = *ma.l_at(w, head);
 #pragma unroll
         for (int jc = 0; jc < kDv / 64; ++jc)
             ov[jc][kg] = *reinterpret_cast<const f32x4 *>(ma.row(w, head) + 4 * cq + 64 * jc);
@@ -867,8 +923,9 @@ void mla_split_kernel(Params p) {
     const int lane = threadIdx.x & 63;
     // Wave-uniform (scalar) so that stage addresses stay in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = blockIdx.x;
-    const int rb0 = (p.y0 + blockIdx.y) * kWaves;
+    int g, grp;
+    range_and_group(blockIdx.x, p.n_groups, gridDim.x / p.n_groups, g, grp);
+    const int rb0 = (p.y0 + grp) * kWaves;
     const int nrb = kMode == kOneBlock ? 1 : kMode == kTwoGroups ? 2 : min(kWaves, p.n_rb - rb0);
     const int nkg = kWaves / nrb;
     const int my_rbl = wave % nrb;
@@ -879,8 +936,17 @@ void mla_split_kernel(Params p) {
     const int tok = rb / hpt;
     const int h0 = (rb % hpt) * 16;
 
-    // Plan (same arithmetic as mla_plan on the host).
-    const int64_t total = plan_total(p, lane);
+    // Plan (same arithmetic as mla_plan on the host).  The lengths of the
+    // first 64 sequences are loaded once, for the total and for the walk
+    // over the sequences below.
+    const int32_t len0 = lane < p.batch ? seq_len(p, lane) : 0;
+    const int64_t incl0 = wave_incl_scan_len(padded_len(len0));
+    int64_t total_l = lane_value(incl0, 63);
+    for (int b0 = 64; b0 < p.batch; b0 += 64) {
+        const int bl = b0 + lane;
+        total_l += lane_value(wave_incl_scan_len(bl < p.batch ? padded_len(seq_len(p, bl)) : 0), 63);
+    }
+    const int64_t total = uniform(total_l);
     const int64_t chunk = plan_chunk(total, p.splits, p.min_chunk);
     const int64_t gs = (int64_t)g * chunk;
     if (gs >= total) return;  // uniform over the workgroup
@@ -891,9 +957,9 @@ void mla_split_kernel(Params p) {
     int64_t base = 0;
     for (int b0 = 0; b0 < p.batch && base < ge; b0 += 64) {
         const int bl = b0 + lane;
-        const int32_t Ll = bl < p.batch ? seq_len(p, bl) : 0;
+        const int32_t Ll = b0 == 0 ? len0 : (bl < p.batch ? seq_len(p, bl) : 0);
         const int64_t lpl = padded_len(Ll);
-        const int64_t incl = wave_incl_scan_i64(lpl, lane) + base;
+        const int64_t incl = (b0 == 0 ? incl0 : wave_incl_scan_len(lpl)) + base;
         const int64_t stl = incl - lpl;
         uint64_t mask = __ballot(bl < p.batch && lpl > 0 && stl < ge && incl > gs);
         const int64_t next_base = lane_value(incl, 63);
@@ -1113,28 +1179,38 @@ void mla_split_kernel(Params p) {
                 wait_vm<0>();
                 bare_barrier();
             } else {
-                // Merge the waves of this segment through LDS.
-                __syncthreads();
-                if (active) {
+                // Merge the waves of this segment through LDS: each wave
+                // puts its O rows and stats into the merge area, then all
+                // threads merge them.
+                auto put_rows = [&](const auto &area) {
                     const int head = lane & 15;
                     const int grp = lane >> 4;
                     float lt = ws.l;
                     lt += __shfl_xor(lt, 16);
                     lt += __shfl_xor(lt, 32);
-                    float *dst = ma.row(wave, head) + 4 * grp;
+                    float *dst = area.row(wave, head) + 4 * grp;
 #pragma unroll
                     for (int ct = 0; ct < kOutTiles; ++ct)
                         *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct];
                     if (grp == 0) {
-                        ma.m[wave * 16 + head] = ws.m;
-                        ma.l[wave * 16 + head] = lt;
+                        *area.m_at(wave, head) = ws.m;
+                        *area.l_at(wave, head) = lt;
                     }
-                }
-                __syncthreads();
-                if constexpr (kMode == kOneBlock)
-                    merge_waves<4>(p, ma, b, rb0, 0, 1, whole, slot);
-                else
+                };
+                if constexpr (kMode == kOneBlock) {
+                    // Into this wave's own ring blocks, which it has finished
+                    // reading: no wait for the other waves first.
+                    const WaveMergeArea wma{stage0_base, stage1_base};
+                    put_rows(wma);
+                    __syncthreads();
+                    merge_waves<4>(p, wma, b, rb0, 0, 1, whole, slot);
+                } else {
+                    // Into the ring, once every wave is done with it.
+                    __syncthreads();
+                    if (active) put_rows(ma);
+                    __syncthreads();
                     for (int rbl = 0; rbl < nrb; ++rbl) merge_waves<2>(p, ma, b, rb0, rbl, nrb, whole, slot);
+                }
                 __syncthreads();
             }
         }
@@ -1210,8 +1286,10 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(Params p) 
         if (threadIdx.x % kCombineQuads == 0 && blockIdx.z == 0) *lrow = -INFINITY;
         return;
     }
-    const int g_first = (int)(st_b / chunk);
-    const int g_last = (int)((st_b + lp - 1) / chunk);
+    // (There are p.splits ranges: the bound keeps every part read inside the
+    // workspace.)
+    const int g_first = (int)min(st_b / chunk, (int64_t)p.splits - 1);
+    const int g_last = (int)min((st_b + lp - 1) / chunk, (int64_t)p.splits - 1);
     if (g_first == g_last) return;  // finished inside one range by the split kernel
 
     // Batches no wider than the parts of the sequence: a wider one would
@@ -1297,17 +1375,20 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool
     // Row-block groups of four (and a last group of three) run the one-group
     // kernel, a last group of two the two-group one and a group of one
     // (s_q * heads = 16, or the last group when n_rb % 4 == 1) the per-wave
-    // one.  Each launch covers groups y0 .. y0 + gridDim.y - 1.
+    // one.  Each launch covers groups y0 .. y0 + n_groups - 1, with
+    // grid_x x n_groups workgroups in one dimension (range_and_group).
     const int rem = n_rb % kWaves;
     const int full = n_rb / kWaves + (rem == 3 ? 1 : 0);
     if (ev) (void)hipEventRecord(ev->split_start, stream);
     hipError_t e = hipSuccess;
     if (full > 0) {
         prm.y0 = 0;
+        prm.n_groups = full;
         if (p_bf16)
-            hipLaunchKernelGGL((mla_split_kernel<kOneGroup, true>), dim3(grid_x, full), dim3(kThreads), 0, stream, prm);
+            hipLaunchKernelGGL((mla_split_kernel<kOneGroup, true>), dim3(grid_x * full), dim3(kThreads), 0, stream,
+                               prm);
         else
-            hipLaunchKernelGGL((mla_split_kernel<kOneGroup, false>), dim3(grid_x, full), dim3(kThreads), 0, stream,
+            hipLaunchKernelGGL((mla_split_kernel<kOneGroup, false>), dim3(grid_x * full), dim3(kThreads), 0, stream,
                                prm);
         e = hipGetLastError();
         if (e != hipSuccess) {
@@ -1317,12 +1398,13 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool
     }
     if (rem == 1 || rem == 2) {
         prm.y0 = n_rb / kWaves;
+        prm.n_groups = 1;
         if (rem == 1)
-            hipLaunchKernelGGL((mla_split_kernel<kOneBlock, false>), dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
+            hipLaunchKernelGGL((mla_split_kernel<kOneBlock, false>), dim3(grid_x), dim3(kThreads), 0, stream, prm);
         else if (p_bf16)
-            hipLaunchKernelGGL((mla_split_kernel<kTwoGroups, true>), dim3(grid_x, 1), dim3(kThreads), 0, stream, prm);
+            hipLaunchKernelGGL((mla_split_kernel<kTwoGroups, true>), dim3(grid_x), dim3(kThreads), 0, stream, prm);
         else
-            hipLaunchKernelGGL((mla_split_kernel<kTwoGroups, false>), dim3(grid_x, 1), dim3(kThreads), 0, stream,
+            hipLaunchKernelGGL((mla_split_kernel<kTwoGroups, false>), dim3(grid_x), dim3(kThreads), 0, stream,
                                prm);
         e = hipGetLastError();
         if (e != hipSuccess) {

@@ -49,6 +49,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -278,6 +279,17 @@ struct BlockCtx {
     int64_t num_pages;
     int32_t last_key;          // L - 1: loads of keys past it are clamped to it
 };
+
+__device__ inline BlockCtx block_ctx(const Params &p, int b, int32_t L) {
+    BlockCtx bc;
+    bc.kv = p.kv;
+    bc.page_size = p.page_size;
+    bc.num_pages = p.num_pages;
+    bc.table_row = p.page_size ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+    bc.seq_base = (int64_t)b * p.kv_capacity;
+    bc.last_key = L - 1;
+    return bc;
+}
 
 // LDS image of one 16-key block (16 latent rows of 72 16-byte chunks):
 // 18 slices of 1 KB.  Slice t = 9h + u holds rows 8h .. 8h+7, chunks
@@ -793,24 +805,43 @@ struct WaveMergeArea {
     __device__ float *l_at(int w, int head) const { return m_at(w, head) + 16; }
 };
 
+// One row block, while the next segment's first blocks land in the stage-0
+// blocks: each wave's rows go through its stage-1 block half a row at a
+// time (256 channels, pitch 260 floats), with the stats after them.
+constexpr int kHalfCols = kDv / 2;
+constexpr int kHalfPitch = kHalfCols + 4;
+static_assert((16 * kHalfPitch + 32) * 4 <= kBlockBytes, "half rows and the stats fit in a block");
+struct HalfMergeArea {
+    char *stage1;
+    __device__ float *row(int w, int head) const {
+        return reinterpret_cast<float *>(stage1 + w * kBlockBytes) + head * kHalfPitch;
+    }
+    __device__ float *m_at(int w, int head) const {
+        return reinterpret_cast<float *>(stage1 + w * kBlockBytes) + 16 * kHalfPitch + head;
+    }
+    __device__ float *l_at(int w, int head) const { return m_at(w, head) + 16; }
+};
+
 // Rows of row block rb0 + rbl from the NKG waves that computed them (waves
 // rbl + nrb kg): the LSE-weighted sum of their O rows, normalized, written
-// as the final rows (whole) or as the segment's part.  Every LDS read is
-// issued before the first is used.  256 threads: 16 heads x 16 quads.
-template <int NKG, typename Area>
+// as the final rows (whole) or as the segment's part.  The area holds
+// channels col0 .. col0 + kCols - 1 of each row (the LSE goes out with
+// col0 = 0).  Every LDS read is issued before the first is used.  256
+// threads: 16 heads x 16 quads.
+template <int NKG, int kCols, typename Area>
 __device__ inline void merge_waves(const Params &p, const Area &ma, int b, int rb0, int rbl, int nrb,
-                                   bool whole, int slot) {
+                                   bool whole, int slot, int col0) {
     const int head = threadIdx.x >> 4;
     const int cq = threadIdx.x & 15;
     float mw[NKG], lw[NKG];
-    f32x4 ov[kDv / 64][NKG];
+    f32x4 ov[kCols / 64][NKG];
 #pragma unroll
     for (int kg = 0; kg < NKG; ++kg) {
         const int w = rbl + nrb * kg;
         mw[kg] = *ma.m_at(w, head);
         lw[kg] = *ma.l_at(w, head);
 #pragma unroll
-        for (int jc = 0; jc < kDv / 64; ++jc)
+        for (int jc = 0; jc < kCols / 64; ++jc)
             ov[jc][kg] = *reinterpret_cast<const f32x4 *>(ma.row(w, head) + 4 * cq + 64 * jc);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -831,15 +862,15 @@ __device__ inline void merge_waves(const Params &p, const Area &ma, int b, int r
     const int64_t row = ((int64_t)b * p.s_q + rbg / hpt) * p.heads + (rbg % hpt) * 16 + head;
     float *orow;
     if (whole) {
-        orow = p.out + row * kDv;
-        if (cq == 0) p.lse[row] = lse2 * kLn2;
+        orow = p.out + row * kDv + col0;
+        if (cq == 0 && col0 == 0) p.lse[row] = lse2 * kLn2;
     } else {
         const int64_t r = ((int64_t)slot * p.n_rb + rbg) * 16 + head;
-        orow = p.part_o + r * kDv;
-        if (cq == 0) p.part_lse[r] = lse2;
+        orow = p.part_o + r * kDv + col0;
+        if (cq == 0 && col0 == 0) p.part_lse[r] = lse2;
     }
 #pragma unroll
-    for (int jc = 0; jc < kDv / 64; ++jc) {
+    for (int jc = 0; jc < kCols / 64; ++jc) {
         f32x4 o = wgt[0] * ov[jc][0];
 #pragma unroll
         for (int kg = 1; kg < NKG; ++kg) o += wgt[kg] * ov[jc][kg];
@@ -886,12 +917,18 @@ __device__ inline void write_rows(const Params &p, const WaveState &ws, int b, i
 //  kOneGroup   nrb = 3, 4: one key group of four waves sharing each 64-key
 //              step through a two-slot ring; all four waves issue a quarter
 //              of each step's loads, and each wave writes its rows itself.
-enum SplitMode { kOneBlock = 0, kTwoGroups = 1, kOneGroup = 2 };
+//  kOneBlockNext  as kOneBlock, for launches where a workgroup may hold
+//              several segments: each wave sends the first block of the
+//              workgroup's next segment before the merge of the current one
+//              (a separate instance: the extra path costs the single-segment
+//              case a little in registers and time).
+enum SplitMode { kOneBlock = 0, kTwoGroups = 1, kOneGroup = 2, kOneBlockNext = 3 };
 
 template <int kMode, bool kHiOnly>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_split_kernel(Params p) {
-    constexpr bool kShared = kMode != kOneBlock;
+    constexpr bool kOne = kMode == kOneBlock || kMode == kOneBlockNext;
+    constexpr bool kShared = !kOne;
     char *stage0_base, *stage1_base;  // kOneBlock, kTwoGroups
     MergeArea ma{};
     if constexpr (kMode == kOneGroup) {
@@ -926,7 +963,7 @@ void mla_split_kernel(Params p) {
     int g, grp;
     range_and_group(blockIdx.x, p.n_groups, gridDim.x / p.n_groups, g, grp);
     const int rb0 = (p.y0 + grp) * kWaves;
-    const int nrb = kMode == kOneBlock ? 1 : kMode == kTwoGroups ? 2 : min(kWaves, p.n_rb - rb0);
+    const int nrb = kOne ? 1 : kMode == kTwoGroups ? 2 : min(kWaves, p.n_rb - rb0);
     const int nkg = kWaves / nrb;
     const int my_rbl = wave % nrb;
     const int my_kg = wave / nrb;
@@ -954,7 +991,23 @@ void mla_split_kernel(Params p) {
 
     const OperandOffsets offs = operand_offsets(lane);
 
+    // One row block: this wave's blocks of a segment that starts at st on
+    // the line and holds Ln keys.  The workgroup's blocks, over all its
+    // segments, go to the waves in turn (turn_now: the wave that takes the
+    // segment's first block), every nkg-th block from kf.
+    auto one_block_share = [&](int64_t st, int32_t Ln, int turn_now, int &kf, int &nm, int &nblk) {
+        const int lo = (int)(max(gs, st) - st);
+        const int hi = (int)(min(ge, st + padded_len(Ln)) - st);
+        const int lim = min(hi, Ln - p.s_q + tok + 1);
+        nblk = lim > lo ? (lim - lo + kKeyBlock - 1) / kKeyBlock : 0;
+        const int off = (my_kg - turn_now) & (kWaves - 1);
+        nm = nblk > off ? (nblk - off + nkg - 1) / nkg : 0;
+        kf = lo + kKeyBlock * off;
+    };
+
     int64_t base = 0;
+    int turn = 0;             // one row block: the wave that takes the next block
+    bool prefetched = false;  // one row block: the segment's first blocks are already in flight
     for (int b0 = 0; b0 < p.batch && base < ge; b0 += 64) {
         const int bl = b0 + lane;
         const int32_t Ll = b0 == 0 ? len0 : (bl < p.batch ? seq_len(p, bl) : 0);
@@ -982,13 +1035,7 @@ void mla_split_kernel(Params p) {
             ws.m = -INFINITY;
             ws.l = 0.f;
 
-            BlockCtx bc;
-            bc.kv = p.kv;
-            bc.page_size = p.page_size;
-            bc.num_pages = p.num_pages;
-            bc.table_row = p.page_size ? p.block_table + (int64_t)b * p.max_pages : nullptr;
-            bc.seq_base = (int64_t)b * p.kv_capacity;
-            bc.last_key = L - 1;
+            const BlockCtx bc = block_ctx(p, b, L);
             const int vis_end = L - p.s_q + tok + 1;  // keys [0, vis_end) visible to this wave
             // This wave's keys.  One row block: every nkg-th 16-key block
             // from kfirst.  Several: the waves of a key group (same keys,
@@ -998,11 +1045,10 @@ void mla_split_kernel(Params p) {
             const bool producer = active && my_rbl == 0;  // loads the keys of its group
             int kfirst, kstep, n_mine, n_iter = 0;
             if constexpr (!kShared) {
-                const int lim = min(seg_hi, vis_end);
-                const int nblk = lim > seg_lo ? (lim - seg_lo + kKeyBlock - 1) / kKeyBlock : 0;
-                n_mine = nblk > my_kg ? (nblk - my_kg + nkg - 1) / nkg : 0;
+                int nblk;
+                one_block_share(st_b, L, turn, kfirst, n_mine, nblk);
                 kstep = kKeyBlock * nkg;
-                kfirst = seg_lo + kKeyBlock * my_kg;
+                turn = (turn + nblk) & (kWaves - 1);
             } else if constexpr (kMode == kOneGroup) {
                 const int tok_last = (rb0 + nrb - 1) / hpt;  // sees the most keys
                 const int lim = min(seg_hi, L - p.s_q + tok_last + 1);
@@ -1034,8 +1080,8 @@ void mla_split_kernel(Params p) {
             // Pages of the next step to issue (shared kernels; kOneGroup: this
             // wave's block in pgA).
             int64_t pgA = 0, pgB = 0;
-            if constexpr (kMode == kOneBlock) {
-                if (n_mine > 0) issue_block(first, bc, kfirst, page_of(bc, kfirst), lane);
+            if constexpr (kOne) {
+                if (n_mine > 0 && !prefetched) issue_block(first, bc, kfirst, page_of(bc, kfirst), lane);
             } else if constexpr (kMode == kTwoGroups) {
                 if (producer && n_mine > 0) {
                     issue_block_buffer(first, bc, kfirst, page_of(bc, kfirst), vrow);
@@ -1182,36 +1228,72 @@ void mla_split_kernel(Params p) {
                 // Merge the waves of this segment through LDS: each wave
                 // puts its O rows and stats into the merge area, then all
                 // threads merge them.
-                auto put_rows = [&](const auto &area) {
+                // put_rows(area, ct0, stats): output tiles ct0 .. ct0 + n - 1
+                // (n = the area's channels / 16) and, with stats, m and l.
+                auto put_rows = [&](const auto &area, int ct0, bool stats) {
+                    constexpr int n = std::is_same_v<std::decay_t<decltype(area)>, HalfMergeArea> ? kOutTiles / 2
+                                                                                                 : kOutTiles;
                     const int head = lane & 15;
                     const int grp = lane >> 4;
-                    float lt = ws.l;
-                    lt += __shfl_xor(lt, 16);
-                    lt += __shfl_xor(lt, 32);
                     float *dst = area.row(wave, head) + 4 * grp;
 #pragma unroll
-                    for (int ct = 0; ct < kOutTiles; ++ct)
-                        *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct];
-                    if (grp == 0) {
-                        *area.m_at(wave, head) = ws.m;
-                        *area.l_at(wave, head) = lt;
+                    for (int ct = 0; ct < n; ++ct)
+                        *reinterpret_cast<f32x4 *>(dst + 16 * ct) = ws.acc[ct0 + ct];
+                    if (stats) {
+                        float lt = ws.l;
+                        lt += __shfl_xor(lt, 16);
+                        lt += __shfl_xor(lt, 32);
+                        if (grp == 0) {
+                            *area.m_at(wave, head) = ws.m;
+                            *area.l_at(wave, head) = lt;
+                        }
                     }
                 };
-                if constexpr (kMode == kOneBlock) {
-                    // Into this wave's own ring blocks, which it has finished
-                    // reading: no wait for the other waves first.
-                    const WaveMergeArea wma{stage0_base, stage1_base};
-                    put_rows(wma);
-                    __syncthreads();
-                    merge_waves<4>(p, wma, b, rb0, 0, 1, whole, slot);
+                if constexpr (kOne) {
+                    // The workgroup's next segment, when it lies in the same
+                    // 64 sequences: this wave sends its first block to its
+                    // stage-0 block now, to land during the merge, and the
+                    // rows go through the stage-1 blocks half a row at a
+                    // time.  The barriers are bare: a full fence would wait
+                    // for those loads.
+                    prefetched = kMode == kOneBlockNext && mask != 0;
+                    if (prefetched) {
+                        const int jn = __builtin_ctzll(mask);
+                        const int32_t Ln = lane_value(Ll, jn);
+                        int kf, nm, nblk;
+                        one_block_share(lane_value(stl, jn), Ln, turn, kf, nm, nblk);
+                        if (nm > 0) {
+                            const BlockCtx bn = block_ctx(p, b0 + jn, Ln);
+                            issue_block(stage0_base + wave * kBlockBytes, bn, kf, page_of(bn, kf), lane);
+                        }
+                        const HalfMergeArea hma{stage1_base};
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            put_rows(hma, half * (kOutTiles / 2), half == 0);
+                            wait_lgkm0();
+                            bare_barrier();
+                            merge_waves<4, kHalfCols>(p, hma, b, rb0, 0, 1, whole, slot, half * kHalfCols);
+                            wait_lgkm0();
+                            bare_barrier();
+                        }
+                    } else {
+                        // Into this wave's own ring blocks, which it has
+                        // finished reading: no wait for the other waves first.
+                        const WaveMergeArea wma{stage0_base, stage1_base};
+                        put_rows(wma, 0, true);
+                        __syncthreads();
+                        merge_waves<4, kDv>(p, wma, b, rb0, 0, 1, whole, slot, 0);
+                        __syncthreads();
+                    }
                 } else {
                     // Into the ring, once every wave is done with it.
                     __syncthreads();
-                    if (active) put_rows(ma);
+                    if (active) put_rows(ma, 0, true);
                     __syncthreads();
-                    for (int rbl = 0; rbl < nrb; ++rbl) merge_waves<2>(p, ma, b, rb0, rbl, nrb, whole, slot);
+                    for (int rbl = 0; rbl < nrb; ++rbl)
+                        merge_waves<2, kDv>(p, ma, b, rb0, rbl, nrb, whole, slot, 0);
+                    __syncthreads();
                 }
-                __syncthreads();
             }
         }
         base = next_base;
@@ -1358,16 +1440,23 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool
     // the combine only when some sequence is split.
     int grid_x = splits;
     bool need_combine = true;
+    bool several_segments = p->batch > 1;  // some workgroup may take more than one sequence
     if (p->seqlens_host) {
         int64_t total = 0;
         for (int b = 0; b < p->batch; ++b) total += padded_len(p->seqlens_host[b]);
         const int64_t chunk = plan_chunk(total, splits, prm.min_chunk);
         grid_x = (int)std::max<int64_t>(1, (total + chunk - 1) / chunk);
+        // A workgroup holds several segments exactly where a sequence with
+        // keys starts inside a range.
         need_combine = false;
+        several_segments = false;
         int64_t st = 0;
-        for (int b = 0; b < p->batch && !need_combine; ++b) {
+        for (int b = 0; b < p->batch; ++b) {
             const int64_t lp = padded_len(p->seqlens_host[b]);
-            need_combine = lp > 0 && st / chunk != (st + lp - 1) / chunk;
+            if (lp > 0) {
+                need_combine = need_combine || st / chunk != (st + lp - 1) / chunk;
+                several_segments = several_segments || st % chunk != 0;
+            }
             st += lp;
         }
     }
@@ -1399,7 +1488,10 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool
     if (rem == 1 || rem == 2) {
         prm.y0 = n_rb / kWaves;
         prm.n_groups = 1;
-        if (rem == 1)
+        if (rem == 1 && several_segments)
+            hipLaunchKernelGGL((mla_split_kernel<kOneBlockNext, false>), dim3(grid_x), dim3(kThreads), 0, stream,
+                               prm);
+        else if (rem == 1)
             hipLaunchKernelGGL((mla_split_kernel<kOneBlock, false>), dim3(grid_x), dim3(kThreads), 0, stream, prm);
         else if (p_bf16)
             hipLaunchKernelGGL((mla_split_kernel<kTwoGroups, true>), dim3(grid_x), dim3(kThreads), 0, stream, prm);

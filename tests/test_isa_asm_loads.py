@@ -38,11 +38,12 @@ def steps_asm(tmp_path_factory):
     return device_asm(tmp_path_factory, libbuild.STEPS_SRC, "steps.s")
 
 
-# Every instance of the split kernel: one row block per workgroup, two key
+# Every instance of the split kernel: one row block per workgroup (also the
+# one that sends the next segment's first blocks before the merge), two key
 # groups, one key group; the shared-step ones also with P as one bf16
 # (MLA_OPT_P_BF16).
 SPLIT_KERNELS = tuple(f"_ZN3mla16mla_split_kernelILi{m}ELb{h}EEEvNS_6ParamsE"
-                      for m, h in ((0, 0), (1, 0), (1, 1), (2, 0), (2, 1)))
+                      for m, h in ((0, 0), (3, 0), (1, 0), (1, 1), (2, 0), (2, 1)))
 
 
 def kernel_body(asm, name):

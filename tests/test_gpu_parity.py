@@ -162,6 +162,37 @@ def test_medium_shapes_against_oracle(ctx, case):
     assert np.array_equal(o, o2) and np.array_equal(l, l2)
 
 
+# More than 64 sequences: the plan and the combine walk the lengths 64 at a
+# time, and a workgroup's segments can run across that boundary.
+MANY = [
+    # (B, s_q, H, page_size, seed)
+    (70, 1, 16, 0, 21),
+    (130, 1, 16, 16, 22),
+    (100, 2, 32, 64, 23),
+    (65, 4, 16, 0, 24),
+]
+
+
+@pytest.mark.parametrize("splits", [0, 7])
+@pytest.mark.parametrize("case", range(len(MANY)))
+def test_more_than_64_sequences(ctx, case, splits):
+    import decode_attention_mla_amd as mla
+
+    B, s_q, H, ps, seed = MANY[case]
+    lens = [int(x) for x in np.random.default_rng(seed).integers(s_q, 400, size=B)]
+    announce(f"many sequences {MANY[case]} splits={splits}")
+    inp = wl.small("many", B, s_q, H, lens, page_size=ps, seed=seed)
+    ctx.set_option(mla.MLA_OPT_NUM_SPLITS, splits)
+    try:
+        o, l = run_gpu(ctx, inp)
+        ro, rl = oracle_of(inp)
+        compare(o, l, ro, rl, str(MANY[case]))
+        o2, l2 = run_gpu(ctx, inp, host_lens=False)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    finally:
+        ctx.set_option(mla.MLA_OPT_NUM_SPLITS, 0)
+
+
 def test_single_key_returns_value_row_exactly(ctx):
     announce("single key")
     inp = wl.small("one", 4, 1, 16, [1, 1, 1, 1], page_size=64, seed=5)

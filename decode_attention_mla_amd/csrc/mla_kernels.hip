@@ -13,13 +13,15 @@
 //
 // Work decomposition (one workgroup = 4 waves of 64 lanes):
 //   * A "row block" is 16 query rows: the 16 heads h0..h0+15 of one token.
-//   * Workgroup (g, y) owns key range g of the split plan (plan.h) and row
-//     blocks 4y .. 4y+3 (nrb of them).  How they share the keys is the
-//     kernel's mode (SplitMode): with one row block the four waves split the
-//     keys, each an independent flash-decoding worker over every 4th 16-key
-//     block with a private LDS ring and no barrier; with two to four the
-//     waves of a key group compute the same 32-key steps for different row
-//     blocks, fed through a shared two-slot LDS ring, one barrier per step.
+//   * A workgroup owns key range g of the split plan (plan.h) and row
+//     blocks 4y .. 4y+3 (nrb of them); range_and_group maps its id to (g, y)
+//     so that the groups of one range share an XCD.  How they share the
+//     keys is the kernel's mode (SplitMode): with one row block the four
+//     waves split the keys, each an independent flash-decoding worker over
+//     every 4th 16-key block with a private LDS ring and no barrier; with
+//     two to four the waves of a key group compute the same 32- or 64-key
+//     steps for different row blocks, fed through a shared two-slot LDS
+//     ring, one barrier per step.
 //   * At the end of a segment (the range's part of one sequence) the waves'
 //     results are merged (through LDS where several waves share a row
 //     block) into the final rows or into a partial for the combine kernel.

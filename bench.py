@@ -670,6 +670,9 @@ def trace_summary(args) -> int:
                  "Command:", "", "```", f"cd /tmp && {shown}", "```", "",
                  "Every dispatch of the run is counted: the clock-settling steps (about one second), the warmup, "
                  "the timed steps and the event-timed repeat.", "",
+                 "`mla_split_kernel<mode, p_bf16>`: mode 0 one row block per workgroup, 1 two key groups, "
+                 "2 one key group of three or four row blocks, 3 one row block that sends the next segment's "
+                 "first block before the merge; p_bf16 is MLA_OPT_P_BF16.", "",
                  "| kernel | calls | mean us | min us | max us | share |", "|---|---|---|---|---|---|"]
         split_rows = []
         for r in rows:

@@ -112,7 +112,7 @@ struct Params {
     int32_t page_size;
     int32_t max_pages;
     int32_t n_rb;      // row blocks: s_q * heads / 16
-    int32_t splits;    // key ranges (gridDim.x of the split kernel when sized blind)
+    int32_t splits;    // key ranges (the split grid holds splits x n_groups workgroups when sized blind)
     int32_t y0;        // first row-block group of the launch
     int32_t n_groups;  // row-block groups in the launch (workgroups: key ranges x n_groups)
     float scale_log2;  // scale * log2(e)

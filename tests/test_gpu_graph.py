@@ -21,15 +21,19 @@ def announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
+# s_q = 2: two row blocks (the two-key-group kernel); s_q = 1: one row block,
+# launched blind with three sequences, so the kernel that sends a
+# workgroup's next segment ahead of the merge.
+@pytest.mark.parametrize("s_q", [2, 1])
 @pytest.mark.parametrize("page_size", [0, 16])
-def test_graph_replays_match_the_oracle(page_size):
+def test_graph_replays_match_the_oracle(page_size, s_q):
     import torch
 
     import decode_attention_mla_amd as mla
 
-    B, s_q, H = 3, 2, 16
+    B, H = 3, 16
     full = [700, 33, 2048]
-    announce(f"graph capture page_size={page_size}")
+    announce(f"graph capture page_size={page_size} s_q={s_q}")
     inp = wl.small("g", B, s_q, H, full, page_size=page_size, seed=11)
     q, kv, bt, lens = to_device(inp)
     stream = torch.cuda.Stream()

@@ -146,6 +146,15 @@ def check_plan(lens, splits, min_chunk):
     assert info["split_sequences"] == sum(1 for ss in per_seq.values() if len(ss) > 1)
     # balance: no group holds more than one chunk of padded keys
     assert max(load.values()) <= chunk
+    # some group holds several segments exactly where a sequence with keys
+    # starts inside a range (the launcher picks the kernel that sends the
+    # next segment's first block ahead by this rule)
+    starts = np.concatenate([[0], np.cumsum(padded)[:-1]])
+    off_boundary = any(p > 0 and st % chunk != 0 for p, st in zip(padded, starts))
+    per_group = {}
+    for s in segs:
+        per_group[s["group"]] = per_group.get(s["group"], 0) + 1
+    assert (max(per_group.values()) > 1) == off_boundary
     return segs, info
 
 

@@ -120,3 +120,32 @@ def test_trace_summary_from_raw_output(tmp_path):
     assert "| void mla::mla_split_kernel<0>(mla::Params) | 10 | 10.00 | 9.00 | 12.00 | 90.9% |" in md
     # 589,824 B in 10 us
     assert "split kernel mean 10.00 us -> 59.0 GB/s" in md
+
+
+def test_committed_bench_line_is_consistent():
+    """The stored default bench line keeps the JSON contract and its own
+    arithmetic: value from bytes and step time, the split kernel's achieved
+    bandwidth from its bytes and mean time, frac = achieved / peak, and the
+    traffic of the counters stored for the current kernels."""
+    import json
+
+    import bench
+
+    with open(os.path.join(ROOT, "profiles", "bench_mla_bs16_ctx65536.json")) as f:
+        d = json.load(f)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["unit"] == "GB/s" and d["higher_is_better"] is True
+    assert d["config"]["workload"] == "mla_bs16_ctx65536"
+    kv = d["config"]["kv_bytes"]
+    assert abs(d["value"] - kv / (d["ms_per_step"] * 1e3) / 1e3) <= 0.01 * d["value"]
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert r["algorithmic_bytes_per_launch"] == kv
+    assert abs(r["achieved"] - kv / r["split_us_mean"] / 1e3) <= 0.001 * r["achieved"]
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) <= 1e-4
+    traffic, rec = bench.stored_traffic("mla_bs16_ctx65536")
+    assert traffic is not None and r["traffic"] == traffic
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["cores"] >= 1 and c["value"] > 0

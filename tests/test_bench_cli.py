@@ -149,3 +149,23 @@ def test_committed_bench_line_is_consistent():
     assert traffic is not None and r["traffic"] == traffic
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["cores"] >= 1 and c["value"] > 0
+
+
+def test_profile_summaries_name_the_current_kernels():
+    """Every stored summary of the attention kernels (traffic, counters,
+    kernel traces, sweep) was taken on the kernel source as it stands: the
+    source hash each one records matches."""
+    import glob
+    import re
+
+    import bench
+
+    sha = bench.kernel_source_hash()
+    found = 0
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            m = re.search(r"[Kk]ernel source sha256 ([0-9a-f]{16})", f.read())
+        if m:
+            found += 1
+            assert sha.startswith(m.group(1)), f"{os.path.basename(path)} is stale: re-take it"
+    assert found >= 16

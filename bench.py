@@ -645,10 +645,13 @@ def trace_summary(args) -> int:
     for name in args.trace_summary.split(","):
         w = wl.WORKLOADS[name]
         kv_bytes = int(wl.draw_seqlens(w).astype("int64").sum()) * wl.D_QK * 2
-        out_dir = os.path.join(args.counters_dir, f"trace_{name}")
+        # With --p-bf16 the traced run uses MLA_OPT_P_BF16 and the summary
+        # is filed under its own name.
+        tag = f"{name}_p_bf16" if args.p_bf16 else name
+        out_dir = os.path.join(args.counters_dir, f"trace_{tag}")
         cmd = ["rocprofv3", "--kernel-trace", "--stats", "-f", "csv", "-d", out_dir, "-o", "run", "--",
                sys.executable, os.path.join(ROOT, "bench.py"), "--workload", name, "--steps", "20",
-               "--warmup", "5", "--no-cpu-baseline"]
+               "--warmup", "5", "--no-cpu-baseline", *(["--p-bf16"] if args.p_bf16 else [])]
         if not args.counters_reuse:
             os.makedirs(out_dir, exist_ok=True)
             print(f"[trace] {' '.join(cmd)}", file=sys.stderr, flush=True)
@@ -665,7 +668,7 @@ def trace_summary(args) -> int:
         rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
         total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
         shown = " ".join(cmd).replace(out_dir, "<out>").replace(sys.executable, "python3").replace(ROOT, "/root/repo")
-        lines = [f"# Kernel trace: {name}", "",
+        lines = [f"# Kernel trace: {name}" + (" with MLA_OPT_P_BF16" if args.p_bf16 else ""), "",
                  f"Source revision: {rev} (kernel source sha256 {sha[:16]}...), MI355X (gfx950), ROCm 7.2.", "",
                  "Command:", "", "```", f"cd /tmp && {shown}", "```", "",
                  "Every dispatch of the run is counted: the clock-settling steps (about one second), the warmup, "
@@ -689,7 +692,7 @@ def trace_summary(args) -> int:
                       f"{mean:.2f} us -> {kv_bytes / mean / 1e3:.1f} GB/s "
                       f"({kv_bytes / mean / 1e3 / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s)."]
         os.makedirs(args.profiles_out, exist_ok=True)
-        with open(os.path.join(args.profiles_out, f"mla_split_{name}_kernel_trace.md"), "w") as fh:
+        with open(os.path.join(args.profiles_out, f"mla_split_{tag}_kernel_trace.md"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
         print(json.dumps({"mode": "trace-summary", "workload": name, "kernels": len(rows)}), flush=True)
     return 0

@@ -18,7 +18,7 @@ import oracle
 import workloads as wl
 from gpu_util import compare, run_gpu
 
-N_CASES = 160
+N_CASES = 600
 MAX_ROW_KEYS = 3_000_000  # bounds the oracle's work per case (rows x keys)
 
 

@@ -77,3 +77,52 @@ def test_random_shapes_against_oracle():
         ctx.set_option(mla.MLA_OPT_NUM_SPLITS, 0)
         ctx.set_option(mla.MLA_OPT_MIN_CHUNK, 0)
         ctx.close()
+
+
+N_MANY = 40
+
+
+def draw_many(i):
+    """Larger batches of short sequences (65-200 of 1-300 keys): the plan and
+    the combine walk the lengths 64 at a time, and most workgroups hold
+    several segments."""
+    rng = np.random.default_rng([4343, i])
+    H = int(rng.choice([16, 32, 64]))
+    s_q = int(rng.integers(1, 3))
+    B = int(rng.integers(65, 201))
+    lens = [int(x) for x in rng.integers(s_q, 301, size=B)]
+    page = int(rng.choice([0, 16, 64]))
+    splits = int(rng.choice([0, 0, 7, 100]))
+    host_lens = bool(rng.integers(0, 2))
+    return dict(B=B, s_q=s_q, H=H, lens=lens, page=page, splits=splits, host_lens=host_lens, seed=6000 + i)
+
+
+@pytest.mark.gpu
+def test_many_short_sequences_against_oracle():
+    import torch
+
+    import decode_attention_mla_amd as mla
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    ctx = mla.Context()
+    try:
+        for i in range(N_MANY):
+            c = draw_many(i)
+            print(f"[many {i}] B={c['B']} s_q={c['s_q']} H={c['H']} page={c['page']} splits={c['splits']} "
+                  f"host_lens={c['host_lens']}", flush=True)
+            inp = wl.small("mn", c["B"], c["s_q"], c["H"], c["lens"], page_size=c["page"], seed=c["seed"])
+            ctx.set_option(mla.MLA_OPT_NUM_SPLITS, c["splits"])
+            o, l = run_gpu(ctx, inp, host_lens=c["host_lens"])
+            ro, rl = oracle.mla_decode(inp.q, inp.kv, inp.block_table, inp.seqlens, inp.scale)
+            compare(o, l, ro, rl, f"many case {i}")
+    finally:
+        ctx.set_option(mla.MLA_OPT_NUM_SPLITS, 0)
+        ctx.close()
+
+
+def test_many_draws_are_within_the_bounds():
+    for i in range(N_MANY):
+        c = draw_many(i)
+        assert 65 <= c["B"] <= 200 and c["H"] % 16 == 0
+        assert all(c["s_q"] <= L <= 300 for L in c["lens"])

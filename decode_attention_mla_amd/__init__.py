@@ -235,8 +235,10 @@ def _need(name, t, dtype, shape=None, ndim=None):
             raise TypeError(f"{name} must have shape {want}, has {list(t.shape)}")
 
 
-def _on_one_device(**tensors):
-    """Every tensor on the same GPU (checked after the shapes)."""
+def _on_one_device(stream, **tensors):
+    """Every tensor on the same GPU as the stream the kernels are launched on
+    (checked after the shapes): the library takes the pointers as they come,
+    so a tensor of another GPU would be read on the wrong device."""
     dev = None
     for name, t in tensors.items():
         if t is None:
@@ -247,6 +249,13 @@ def _on_one_device(**tensors):
             dev = t.device
         elif t.device != dev:
             raise TypeError(f"{name} is on {t.device}, the other tensors on {dev}")
+    if stream is not None and dev is not None and stream.device != dev:
+        raise TypeError(f"the tensors are on {dev}, the stream the kernels run on is on {stream.device}")
+
+
+def _stream_of(ctx):
+    """The stream a context launches on (None without a context)."""
+    return getattr(ctx, "stream", None)
 
 
 def _cache_layout(kv_cache, block_table, batch, kv_capacity):
@@ -306,7 +315,8 @@ def mla_decode(ctx: Context, q, kv_cache, block_table, seqlens, scale: float, ou
         _need("out", out, torch.float32, (B, s_q, H, HEAD_DIM_V))
     if lse is not None:
         _need("lse", lse, torch.float32, (B, s_q, H))
-    _on_one_device(q=q, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens, out=out, lse=lse)
+    _on_one_device(_stream_of(ctx), q=q, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens,
+                   out=out, lse=lse)
     if out is None:
         out = torch.empty((B, s_q, H, HEAD_DIM_V), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -327,8 +337,8 @@ def mla_decode_noalloc(q, kv_cache, block_table, seqlens, scale: float, out, lse
                        stream=None):
     """mla_decode without a context and without any allocation: the split
     partials go to the library's static scratch array.  out and lse must be
-    given (shapes as for ``mla_decode``); `stream` defaults to torch's
-    current stream.  Returns (out, lse)."""
+    given (shapes as for ``mla_decode``), on the current device; `stream`
+    defaults to torch's current stream.  Returns (out, lse)."""
     import torch
 
     _need("q", q, torch.bfloat16, (None, None, None, HEAD_DIM_QK))
@@ -342,7 +352,12 @@ def mla_decode_noalloc(q, kv_cache, block_table, seqlens, scale: float, out, lse
         raise TypeError("mla_decode_noalloc writes into the caller's out and lse: pass both")
     _need("out", out, torch.float32, (B, s_q, H, HEAD_DIM_V))
     _need("lse", lse, torch.float32, (B, s_q, H))
-    _on_one_device(q=q, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens, out=out, lse=lse)
+    _on_one_device(stream, q=q, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens, out=out,
+                   lse=lse)
+    # The library takes the scratch array of the current device.
+    if q.device.index != torch.cuda.current_device():
+        raise TypeError(f"the tensors are on {q.device}, the current device is "
+                        f"cuda:{torch.cuda.current_device()}")
     if stream is None:
         stream = torch.cuda.current_stream()
     pr, keep = make_problem(B, s_q, H, page_size, cap, num_pages, max_pages, host)
@@ -377,7 +392,8 @@ def mla_append_kv(ctx: Context, new_rows, kv_cache, block_table, seqlens,
     if seqlens.shape[0] < B:
         raise TypeError(f"seqlens has {seqlens.shape[0]} entries for {B} sequences")
     host = _host_lengths(seqlens_host, B)
-    _on_one_device(new_rows=new_rows, kv_cache=kv_cache, block_table=block_table, seqlens=seqlens)
+    _on_one_device(_stream_of(ctx), new_rows=new_rows, kv_cache=kv_cache, block_table=block_table,
+                   seqlens=seqlens)
     pr, keep = make_problem(B, s_q, 1, page_size, cap, num_pages, max_pages, host)
     pr.head_dim_qk = dqk
     bt_ptr = None if block_table is None else block_table.data_ptr()
@@ -402,7 +418,7 @@ def mla_absorb_q(ctx: Context, q_nope, q_rope, w_uk, q_out=None):
     rows = int(np.prod(lead)) if len(lead) else 1
     if q_out is not None:
         _need("q_out", q_out, torch.bfloat16, (*lead, H, HEAD_DIM_QK))
-    _on_one_device(q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, q_out=q_out)
+    _on_one_device(_stream_of(ctx), q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, q_out=q_out)
     if q_out is None:
         q_out = torch.empty((*lead, H, HEAD_DIM_QK), dtype=torch.bfloat16, device=q_nope.device)
     _check(load().mla_absorb_q(ctx.handle, q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(),
@@ -423,7 +439,7 @@ def mla_project_out(ctx: Context, o, w_uv, out=None):
     rows = int(np.prod(lead)) if len(lead) else 1
     if out is not None:
         _need("out", out, torch.float32, (*lead, H, d_v))
-    _on_one_device(o=o, w_uv=w_uv, out=out)
+    _on_one_device(_stream_of(ctx), o=o, w_uv=w_uv, out=out)
     if out is None:
         out = torch.empty((*lead, H, d_v), dtype=torch.float32, device=o.device)
     _check(load().mla_project_out(ctx.handle, o.data_ptr(), w_uv.data_ptr(), out.data_ptr(),

@@ -119,3 +119,21 @@ def test_absorb_and_project_checks():
         mla.mla_project_out(None, o, z((16, 128, 576), bf))
     with pytest.raises(TypeError, match="out must have shape"):
         mla.mla_project_out(None, o, wv, out=z((4, 16, 64), f32))
+
+
+class _OnDevice:
+    """Stand-in for a tensor or a stream: only its device is read."""
+
+    def __init__(self, dev):
+        self.device = torch.device(dev)
+
+
+def test_tensors_must_sit_on_the_launch_stream_device():
+    # The check itself, with stand-ins (this host has no GPU): tensors of one
+    # GPU launched on another GPU's stream are refused, as are mixed GPUs.
+    with pytest.raises(TypeError, match="the stream the kernels run on is on cuda:1"):
+        mla._on_one_device(_OnDevice("cuda:1"), q=_OnDevice("cuda:0"), out=_OnDevice("cuda:0"))
+    with pytest.raises(TypeError, match="out is on cuda:1"):
+        mla._on_one_device(_OnDevice("cuda:0"), q=_OnDevice("cuda:0"), out=_OnDevice("cuda:1"))
+    mla._on_one_device(_OnDevice("cuda:0"), q=_OnDevice("cuda:0"), lse=None)
+    mla._on_one_device(None, q=_OnDevice("cuda:1"))

@@ -2,7 +2,8 @@
 C ABI: against mla_decode and against the fp64 oracle, on two calls in a
 row, the second smaller, so that the second reads a scratch array that still
 holds the first call's partials; then a problem whose partials need fewer
-key ranges than the default plan, and one too large for the array.
+key ranges than the default plan, one too large for the array, and the call
+captured in a HIP graph and replayed.
 
 Bar: the O/LSE bar of the parity tests (O RMSE <= 1e-4, max-abs <= 1e-3,
 LSE max-abs <= 1e-4) against the oracle, and equality with mla_decode's
@@ -116,3 +117,48 @@ def test_too_large_is_refused_before_any_launch(mla):
     assert "scratch" in str(ei.value)
     torch.cuda.synchronize()
     assert torch.isnan(out).all() and torch.isnan(lse).all()
+
+
+def test_graph_replays_of_the_noalloc_call(mla):
+    """The call captured in a HIP graph (device lengths only, so nothing on
+    the host reads them) and replayed with new lengths and queries written in
+    place; between replays an eager call of another shape overwrites the
+    scratch array.  Every replay and every eager call against the oracle."""
+    import torch
+
+    B, s_q, H = 3, 1, 16
+    full = [700, 33, 2048]
+    announce("noalloc graph capture")
+    inp = wl.small("nag", B, s_q, H, full, page_size=16, seed=703)
+    other = wl.small("nag2", 2, 2, 16, [1200, 90], page_size=0, seed=704)
+    q, kv, bt, lens = to_device(inp)
+    out = torch.full((B, s_q, H, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, s_q, H), float("nan"), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        mla.mla_decode_noalloc(q, kv, bt, lens, inp.scale, out, lse, stream=stream)  # warm-up
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        mla.mla_decode_noalloc(q, kv, bt, lens, inp.scale, out, lse, stream=stream)
+
+    rng = np.random.default_rng(705)
+    for rep, new_lens in enumerate([full, [2, 33, 1500], [640, 17, 2047], [699, 2, 64]]):
+        # Lengths only shrink, so every key read is a real cache row.
+        inp.seqlens[:] = new_lens
+        inp.q[:] = wl.f32_to_bf16_bits(rng.standard_normal(inp.q.shape).astype(np.float32))
+        lens.copy_(torch.from_numpy(inp.seqlens))
+        q.copy_(torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16))
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, rl = oracle.mla_decode(inp.q, inp.kv, inp.block_table, inp.seqlens, inp.scale)
+        compare(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                ro, rl, f"noalloc replay {rep} lens={new_lens}")
+        # An eager call of another shape between replays (same scratch array).
+        oe, le = run_noalloc(mla, other)
+        roe, rle = oracle.mla_decode(other.q, other.kv, other.block_table, other.seqlens, other.scale)
+        compare(oe, le, roe, rle, f"noalloc eager {rep}")

@@ -216,3 +216,58 @@ def test_growth_is_refused_during_capture_and_keeps_earlier_graphs_valid(mla):
     finally:
         torch.cuda.synchronize()
         ctx.close()
+
+
+def test_two_contexts_on_two_streams_overlap(mla):
+    """Two contexts, each on a stream of its own (default priority), called
+    in turn with no synchronization between the calls, so that their kernels
+    may run at the same time: one on the library's own workspace, one on a
+    caller's torch buffer.  Each context's partials stay its own: every
+    result against the oracle and, bit for bit, against the same call made
+    alone."""
+    import torch
+
+    announce("two contexts on two streams")
+    ia = wl.small("s2a", 4, 1, 16, [3000, 5000, 100, 64], page_size=0, seed=811)
+    ib = wl.small("s2b", 2, 4, 16, [2000, 4100], page_size=64, seed=812)
+    da, db = to_device(ia), to_device(ib)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ca, cb = mla.Context(stream=sa), mla.Context(stream=sb)
+    try:
+        ca.reserve(1, 16)
+        buf = cb.allocate_workspace(4, 16)
+        torch.cuda.synchronize()
+        outs = []
+        for rep in range(3):
+            oa = torch.full((4, 1, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+            la = torch.full((4, 1, 16), float("nan"), dtype=torch.float32, device="cuda")
+            ob = torch.full((2, 4, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+            lb = torch.full((2, 4, 16), float("nan"), dtype=torch.float32, device="cuda")
+            sa.wait_stream(torch.cuda.current_stream())
+            sb.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(sa):
+                mla.mla_decode(ca, *da, ia.scale, out=oa, lse=la, seqlens_host=ia.seqlens)
+            with torch.cuda.stream(sb):
+                mla.mla_decode(cb, *db, ib.scale, out=ob, lse=lb, seqlens_host=ib.seqlens)
+            outs.append((oa, la, ob, lb))
+        torch.cuda.synchronize()
+        ra = oracle.mla_decode(ia.q, ia.kv, ia.block_table, ia.seqlens, ia.scale)
+        rb = oracle.mla_decode(ib.q, ib.kv, ib.block_table, ib.seqlens, ib.scale)
+        alone = mla.Context()
+        try:
+            aa = run_gpu(alone, ia, dev=da)
+            ab = run_gpu(alone, ib, dev=db)
+        finally:
+            alone.close()
+        for rep, (oa, la, ob, lb) in enumerate(outs):
+            ga = (oa.cpu().numpy().astype(np.float64), la.cpu().numpy().astype(np.float64))
+            gb = (ob.cpu().numpy().astype(np.float64), lb.cpu().numpy().astype(np.float64))
+            compare(*ga, *ra, f"stream a, call {rep}")
+            compare(*gb, *rb, f"stream b, call {rep}")
+            assert np.array_equal(ga[0], aa[0]) and np.array_equal(ga[1], aa[1]), f"stream a, call {rep}"
+            assert np.array_equal(gb[0], ab[0]) and np.array_equal(gb[1], ab[1]), f"stream b, call {rep}"
+        del buf
+    finally:
+        torch.cuda.synchronize()
+        ca.close()
+        cb.close()

@@ -58,7 +58,8 @@ class PlanSegment(ctypes.Structure):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int64), ("total_keys", ctypes.c_int64),
-                ("active_groups", ctypes.c_int32), ("split_sequences", ctypes.c_int32)]
+                ("active_groups", ctypes.c_int32), ("split_sequences", ctypes.c_int32),
+                ("seq_gap", ctypes.c_int64)]
 
 
 _lib = None
@@ -143,7 +144,8 @@ def mla_plan(seqlens: Sequence[int], num_splits: int, min_chunk: int = 64):
     out = [dict(group=s.group, seq=s.seq, key_begin=s.key_begin, key_end=s.key_end, slot=s.slot)
            for s in segs[: n.value]]
     return out, dict(chunk=info.chunk, total_keys=info.total_keys,
-                     active_groups=info.active_groups, split_sequences=info.split_sequences)
+                     active_groups=info.active_groups, split_sequences=info.split_sequences,
+                     seq_gap=info.seq_gap)
 
 
 class Context:

@@ -98,9 +98,8 @@ int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits, int
     mla_host::thread_error().clear();
     if (!seqlens_host || batch < 1 || num_splits < 1 || !n_segs)
         return fail(nullptr, MLA_ERR_INVALID_ARG, "mla_plan: bad arguments");
-    int64_t total = 0;
-    for (int b = 0; b < batch; ++b) total += padded_len(seqlens_host[b] < 0 ? 0 : seqlens_host[b]);
-    const int64_t chunk = plan_chunk(total, num_splits, min_chunk);
+    const HostLine ln = host_plan_line(seqlens_host, batch, num_splits, min_chunk);
+    const int64_t total = ln.total, chunk = ln.chunk;
     int32_t count = 0, split_seqs = 0;
     int64_t st = 0;
     for (int b = 0; b < batch; ++b) {
@@ -121,7 +120,7 @@ int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits, int
             }
             ++count;
         }
-        st += lp;
+        st += lp + ln.gap;
     }
     *n_segs = count;
     if (info) {
@@ -129,6 +128,7 @@ int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits, int
         info->total_keys = total;
         info->active_groups = (int32_t)((total + chunk - 1) / chunk);
         info->split_sequences = split_seqs;
+        info->seq_gap = ln.gap;
     }
     if (segs && count > max_segs)
         return fail(nullptr, MLA_ERR_INVALID_ARG, "mla_plan: %d segments, room for %d", count, max_segs);

@@ -115,6 +115,8 @@ struct Params {
     int32_t splits;    // key ranges (the split grid holds splits x n_groups workgroups when sized blind)
     int32_t y0;        // first row-block group of the launch
     int32_t n_groups;  // row-block groups in the launch (workgroups: key ranges x n_groups)
+    int32_t line_gap;  // the plan's line keys after each sequence, from the host lengths;
+                       // -1 without them (every workgroup then works it out)
     float scale_log2;  // scale * log2(e)
 };
 
@@ -192,25 +194,72 @@ __device__ inline int32_t seq_len(const Params &p, int b) {
     return clamp_len(p.seqlens[b], p.capacity);
 }
 
-// Where sequence b lies on the line of padded keys: its start, its padded
-// length, and the total over all sequences (every lane gets all three).
-// One length load per lane per 64 sequences and one prefix sum of them.
-__device__ inline void line_position(const Params &p, int b, int lane, int64_t &total,
-                                     int64_t &start, int64_t &len) {
+// Length of sequence b0 + lane (0 past the batch); len0 holds it for the
+// first 64 sequences, loaded once.
+__device__ inline int32_t lane_len(const Params &p, int b0, int lane, int32_t len0) {
+    const int bl = b0 + lane;
+    return b0 == 0 ? len0 : (bl < p.batch ? seq_len(p, bl) : 0);
+}
+
+// The plan's line, the same arithmetic as host_plan_line: the padded lengths
+// laid end to end, cut into p.splits ranges of `chunk` keys; when that line
+// starts some sequence with keys inside a range, every sequence with keys is
+// followed by kSeqGap line keys that hold no key, and the ranges are cut
+// from that line.  len0: the lane's length among the first 64 sequences (0
+// past the batch).
+struct Line {
+    int64_t total;  // keys on the line, gaps included
+    int64_t chunk;  // keys per range
+    int64_t gap;    // line keys after each sequence with keys: 0 or kSeqGap
+};
+
+// The gap of the line.  A launch with host lengths passes the host's choice
+// (p.line_gap); without them every workgroup makes it from two passes over
+// the lengths: the plain line's range size, then whether a sequence with keys
+// starts inside one of its ranges.
+__device__ inline int64_t plan_gap(const Params &p, int lane, int32_t len0) {
+    if (p.line_gap >= 0) return p.line_gap;
+    int64_t total = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64)
+        total += lane_value(wave_incl_scan_len(padded_len(lane_len(p, b0, lane, len0))), 63);
+    const int64_t chunk0 = plan_chunk(uniform(total), p.splits, p.min_chunk);
+    bool inside = false;
+    int64_t base = 0;
+    for (int b0 = 0; b0 < p.batch && !inside; b0 += 64) {
+        const int64_t lp = padded_len(lane_len(p, b0, lane, len0));
+        const int64_t incl = wave_incl_scan_len(lp) + base;
+        inside = __ballot(lp > 0 && (incl - lp) % chunk0 != 0) != 0;
+        base = lane_value(incl, 63);
+    }
+    return inside ? kSeqGap : 0;
+}
+
+// Line keys of a sequence of padded length lp.
+__device__ inline int64_t line_keys(int64_t lp, int64_t gap) { return lp > 0 ? lp + gap : 0; }
+
+// The line, and where sequence b lies on it: its start and its padded length
+// (every lane gets all of them; b < 0: none).  One pass over the lengths once
+// the gap is known.
+__device__ inline Line line_position(const Params &p, int b, int lane, int32_t len0, int64_t &start,
+                                     int64_t &len) {
+    Line ln;
+    ln.gap = plan_gap(p, lane, len0);
     int64_t t = 0, s = 0, l = 0;
     for (int b0 = 0; b0 < p.batch; b0 += 64) {
-        const int bl = b0 + lane;
-        const int64_t lpl = bl < p.batch ? padded_len(seq_len(p, bl)) : 0;
-        const int64_t incl = wave_incl_scan_len(lpl);
+        const int64_t lp = padded_len(lane_len(p, b0, lane, len0));
+        const int64_t lnl = line_keys(lp, ln.gap);
+        const int64_t incl = wave_incl_scan_len(lnl);
         if (b >= b0 && b < b0 + 64) {
-            l = lane_value(lpl, b - b0);
-            s = t + lane_value(incl, b - b0) - l;
+            l = lane_value(lp, b - b0);
+            s = t + lane_value(incl, b - b0) - lane_value(lnl, b - b0);
         }
         t += lane_value(incl, 63);
     }
-    total = uniform(t);
+    ln.total = uniform(t);
+    ln.chunk = plan_chunk(ln.total, p.splits, p.min_chunk);
     start = uniform(s);
     len = uniform(l);
+    return ln;
 }
 
 __device__ inline uint16_t bf16_bits(float x) {
@@ -976,14 +1025,15 @@ void mla_split_kernel(Params p) {
     const int h0 = (rb % hpt) * 16;
 
     // Plan (same arithmetic as mla_plan on the host).  The lengths of the
-    // first 64 sequences are loaded once, for the total and for the walk
+    // first 64 sequences are loaded once, for the line and for the walk
     // over the sequences below.
     const int32_t len0 = lane < p.batch ? seq_len(p, lane) : 0;
-    const int64_t incl0 = wave_incl_scan_len(padded_len(len0));
+    const int64_t gap = plan_gap(p, lane, len0);
+    const int64_t incl0 = wave_incl_scan_len(line_keys(padded_len(len0), gap));
     int64_t total_l = lane_value(incl0, 63);
     for (int b0 = 64; b0 < p.batch; b0 += 64) {
         const int bl = b0 + lane;
-        total_l += lane_value(wave_incl_scan_len(bl < p.batch ? padded_len(seq_len(p, bl)) : 0), 63);
+        total_l += lane_value(wave_incl_scan_len(line_keys(bl < p.batch ? padded_len(seq_len(p, bl)) : 0, gap)), 63);
     }
     const int64_t total = uniform(total_l);
     const int64_t chunk = plan_chunk(total, p.splits, p.min_chunk);
@@ -1011,12 +1061,13 @@ void mla_split_kernel(Params p) {
     int turn = 0;             // one row block: the wave that takes the next block
     bool prefetched = false;  // one row block: the segment's first blocks are already in flight
     for (int b0 = 0; b0 < p.batch && base < ge; b0 += 64) {
-        const int bl = b0 + lane;
-        const int32_t Ll = b0 == 0 ? len0 : (bl < p.batch ? seq_len(p, bl) : 0);
+        const int32_t Ll = lane_len(p, b0, lane, len0);
         const int64_t lpl = padded_len(Ll);
-        const int64_t incl = (b0 == 0 ? incl0 : wave_incl_scan_len(lpl)) + base;
-        const int64_t stl = incl - lpl;
-        uint64_t mask = __ballot(bl < p.batch && lpl > 0 && stl < ge && incl > gs);
+        const int64_t lnl = line_keys(lpl, gap);
+        const int64_t incl = (b0 == 0 ? incl0 : wave_incl_scan_len(lnl)) + base;
+        const int64_t stl = incl - lnl;
+        // Sequences with keys in this range (a gap holds none).
+        uint64_t mask = __ballot(lpl > 0 && stl < ge && stl + lpl > gs);
         const int64_t next_base = lane_value(incl, 63);
 
         while (mask) {
@@ -1357,9 +1408,9 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(Params p) 
     const int head = threadIdx.x / kCombineQuads;
     const int c = blockIdx.z * kCombineChannels + 4 * (threadIdx.x % kCombineQuads);
 
-    int64_t total, st_b, lp;
-    line_position(p, b, lane, total, st_b, lp);
-    const int64_t chunk = plan_chunk(total, p.splits, p.min_chunk);
+    int64_t st_b, lp;
+    const int32_t len0 = lane < p.batch ? seq_len(p, lane) : 0;
+    const int64_t chunk = line_position(p, b, lane, len0, st_b, lp).chunk;
     const int hpt = p.heads >> 4;
     const int t = rb / hpt;
     const int hh = (rb % hpt) * 16 + head;
@@ -1437,6 +1488,7 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool
     prm.n_rb = n_rb;
     prm.splits = splits;
     prm.scale_log2 = scale * kLog2e;
+    prm.line_gap = -1;
 
     // Launch sizes: with host lengths, only the ranges that hold keys, and
     // the combine only when some sequence is split.
@@ -1444,12 +1496,12 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool
     bool need_combine = true;
     bool several_segments = p->batch > 1;  // some workgroup may take more than one sequence
     if (p->seqlens_host) {
-        int64_t total = 0;
-        for (int b = 0; b < p->batch; ++b) total += padded_len(p->seqlens_host[b]);
-        const int64_t chunk = plan_chunk(total, splits, prm.min_chunk);
+        const HostLine ln = host_plan_line(p->seqlens_host, p->batch, splits, prm.min_chunk);
+        const int64_t total = ln.total, chunk = ln.chunk;
+        prm.line_gap = (int32_t)ln.gap;
         grid_x = (int)std::max<int64_t>(1, (total + chunk - 1) / chunk);
-        // A workgroup holds several segments exactly where a sequence with
-        // keys starts inside a range.
+        // A workgroup can hold several segments only where a sequence with
+        // keys starts inside a range (without gaps, exactly there).
         need_combine = false;
         several_segments = false;
         int64_t st = 0;
@@ -1458,8 +1510,8 @@ hipError_t launch_decode(hipStream_t stream, int splits, int64_t min_chunk, bool
             if (lp > 0) {
                 need_combine = need_combine || st / chunk != (st + lp - 1) / chunk;
                 several_segments = several_segments || st % chunk != 0;
+                st += lp + ln.gap;
             }
-            st += lp;
         }
     }
 

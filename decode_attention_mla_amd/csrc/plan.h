@@ -3,7 +3,10 @@
 //
 // The keys of all sequences are laid end to end, each sequence padded to a
 // multiple of kKeyBlock, and the line is cut into `splits` equal ranges of
-// `chunk` keys.  Workgroup g owns range [g*chunk, (g+1)*chunk).  A range
+// `chunk` keys.  When that line would start some sequence inside a range,
+// each sequence with keys is followed by kSeqGap line keys that hold no key,
+// and the ranges are cut from that line instead.  Workgroup g owns range
+// [g*chunk, (g+1)*chunk).  A range
 // meets a sequence in a segment.  A sequence inside one range is finished by
 // that workgroup; otherwise every segment writes a partial (normalized O and
 // log2-domain LSE) into slot 2*g + (segment does not start the range) and the
@@ -14,6 +17,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "mla_decode.h"
 
 namespace mla {
 
@@ -33,6 +38,44 @@ __host__ __device__ inline int64_t plan_chunk(int64_t total, int32_t splits, int
     int64_t c = per > min_chunk ? per : min_chunk;
     c = (c + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
     return c > 0 ? c : kChunkAlign;
+}
+
+// Line keys after every sequence with keys when the plain line would start
+// some sequence inside a range.  A range that holds several segments pays a
+// fixed cost for each one after the first (the merge of the one before, the
+// query load, the refill of the pipeline), about what its workgroup streams
+// of this many keys in the meantime, so such a range takes fewer real keys.
+constexpr int64_t kSeqGap = MLA_PLAN_SEQ_GAP;
+static_assert(kSeqGap % kKeyBlock == 0, "sequences keep starting on a block boundary");
+
+// The line as the host evaluates it from host lengths (negative lengths count
+// as empty); every workgroup evaluates the same from the device lengths.
+struct HostLine {
+    int64_t total;  // keys on the line, gaps included
+    int64_t chunk;  // keys per range
+    int64_t gap;    // line keys after each sequence with keys: 0 or kSeqGap
+};
+
+inline HostLine host_plan_line(const int32_t *lens, int32_t batch, int32_t splits, int64_t min_chunk) {
+    int64_t total = 0, with_keys = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t lp = padded_len(lens[b] < 0 ? 0 : lens[b]);
+        total += lp;
+        with_keys += lp > 0 ? 1 : 0;
+    }
+    const int64_t chunk0 = plan_chunk(total, splits, min_chunk);
+    bool inside = false;
+    int64_t st = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t lp = padded_len(lens[b] < 0 ? 0 : lens[b]);
+        inside = inside || (lp > 0 && st % chunk0 != 0);
+        st += lp;
+    }
+    HostLine ln;
+    ln.gap = inside ? kSeqGap : 0;
+    ln.total = total + ln.gap * with_keys;
+    ln.chunk = inside ? plan_chunk(ln.total, splits, min_chunk) : chunk0;
+    return ln;
 }
 
 // Partial slot of the segment that sequence starting at `seq_start` has in

@@ -49,6 +49,11 @@ typedef enum {
 #define MLA_HEAD_DIM_V 512
 /* Keys per kernel block: page sizes must be multiples of it. */
 #define MLA_KEY_BLOCK 16
+/* Line keys the split plan charges to the end of every sequence with keys
+ * when, without them, some sequence would start inside a key range (see
+ * mla_plan): a range that holds several segments pays a fixed cost for each
+ * (merge, query load, pipeline refill), so it takes fewer real keys. */
+#define MLA_PLAN_SEQ_GAP 128
 
 /*
  * Sizes of one decode call (all counts in elements).
@@ -252,19 +257,23 @@ int mla_validate(const void *q, const void *kv_cache, const int32_t *block_table
 
 /*
  * The split-KV plan, evaluated on the host exactly as every workgroup
- * evaluates it on the device.  The keys of all sequences are laid end to end,
- * each sequence padded to a multiple of MLA_KEY_BLOCK; the line is cut into
- * `num_splits` equal ranges of `chunk` keys (a multiple of MLA_KEY_BLOCK, at least
- * `min_chunk`), and workgroup g takes range g.  A workgroup range meets a
- * sequence in a segment; a sequence that lies inside one range is finished
- * there, otherwise each segment writes a partial result into slot
- * 2*g + (segment does not start the range) and a merge combines them.
+ * evaluates it on the device.  The keys of all sequences are laid end to end
+ * on a line, each sequence padded to a multiple of MLA_KEY_BLOCK; the line is
+ * cut into `num_splits` equal ranges of `chunk` keys (a multiple of
+ * MLA_KEY_BLOCK, at least `min_chunk`), and workgroup g takes range g.  When
+ * that line would start some sequence with keys inside a range, every
+ * sequence with keys is followed instead by MLA_PLAN_SEQ_GAP line keys that
+ * hold no key, and the ranges are cut from that longer line.  A workgroup
+ * range meets a sequence in a segment; a sequence that lies inside one range
+ * is finished there, otherwise each segment writes a partial result into
+ * slot 2*g + (segment does not start the range) and a merge combines them.
  *
  *  seqlens_host  host int32 [batch].
  *  segs          host output, room for max_segs segments (may be NULL to
  *                count only); *n_segs receives the total count.
- *  info          host output: chunk, total padded keys, active workgroups,
- *                number of sequences that need the merge.
+ *  info          host output: chunk, keys on the line, active workgroups,
+ *                number of sequences that need the merge, and the line keys
+ *                after each sequence (0 or MLA_PLAN_SEQ_GAP).
  */
 typedef struct {
     int32_t group;     /* workgroup (key range) index */
@@ -276,9 +285,10 @@ typedef struct {
 
 typedef struct {
     int64_t chunk;
-    int64_t total_keys;
+    int64_t total_keys;      /* keys on the line, gaps included */
     int32_t active_groups;
     int32_t split_sequences;
+    int64_t seq_gap;         /* line keys after each sequence with keys */
 } mla_plan_info;
 
 int mla_plan(const int32_t *seqlens_host, int32_t batch, int32_t num_splits,

@@ -112,12 +112,34 @@ def test_validation_errors(kw, code, needle):
 
 # --- the split plan -------------------------------------------------------------
 
+def range_keys(total, splits, min_chunk):
+    """Keys per range for a line of `total` keys: an equal share rounded up
+    to a block, at least min_chunk."""
+    c = max(-(-total // splits), min_chunk)
+    return max(16, -(-c // 16) * 16)
+
+
+def expected_line(padded, splits, min_chunk):
+    """(line keys, keys per range, gap): the plain line of padded lengths,
+    or, when it starts a sequence with keys inside a range, the line with
+    MLA_PLAN_SEQ_GAP keys after every sequence with keys."""
+    total = sum(padded)
+    chunk = range_keys(total, splits, min_chunk)
+    starts = np.concatenate([[0], np.cumsum(padded)[:-1]])
+    if not any(p > 0 and st % chunk != 0 for p, st in zip(padded, starts)):
+        return total, chunk, 0
+    gap = declared_constants()["MLA_PLAN_SEQ_GAP"]
+    total += gap * sum(1 for p in padded if p > 0)
+    return total, range_keys(total, splits, min_chunk), gap
+
+
 def check_plan(lens, splits, min_chunk):
     segs, info = mla.mla_plan(lens, splits, min_chunk)
     chunk = info["chunk"]
     assert chunk % 16 == 0 and chunk >= min_chunk
     padded = [(int(L) + 15) // 16 * 16 for L in lens]
-    assert info["total_keys"] == sum(padded)
+    total, want_chunk, gap = expected_line(padded, splits, min_chunk)
+    assert (info["total_keys"], chunk, info["seq_gap"]) == (total, want_chunk, gap)
     assert info["active_groups"] <= splits
     # every real key covered exactly once, segments inside one sequence
     cover = [np.zeros(int(L), np.int32) for L in lens]
@@ -146,15 +168,24 @@ def check_plan(lens, splits, min_chunk):
     assert info["split_sequences"] == sum(1 for ss in per_seq.values() if len(ss) > 1)
     # balance: no group holds more than one chunk of padded keys
     assert max(load.values()) <= chunk
-    # some group holds several segments exactly where a sequence with keys
-    # starts inside a range (the launcher picks the kernel that sends the
-    # next segment's first block ahead by this rule)
-    starts = np.concatenate([[0], np.cumsum(padded)[:-1]])
-    off_boundary = any(p > 0 and st % chunk != 0 for p, st in zip(padded, starts))
+    # every segment where the line puts it: sequence b starts after the
+    # padded keys and gaps of the sequences before it
+    line_starts = np.concatenate([[0], np.cumsum([p + (gap if p > 0 else 0) for p in padded])[:-1]])
+    for s in segs:
+        st = int(line_starts[s["seq"]])
+        assert s["group"] * chunk <= st + s["key_begin"] < (s["group"] + 1) * chunk
+    # some group holds several segments only where a sequence with keys
+    # starts inside a range, and without gaps exactly there (the launcher
+    # picks the kernel that sends the next segment's first block ahead by
+    # this rule)
+    off_boundary = any(p > 0 and st % chunk != 0 for p, st in zip(padded, line_starts))
     per_group = {}
     for s in segs:
         per_group[s["group"]] = per_group.get(s["group"], 0) + 1
-    assert (max(per_group.values()) > 1) == off_boundary
+    several = max(per_group.values()) > 1
+    assert off_boundary if several else True
+    if gap == 0:
+        assert several == off_boundary
     return segs, info
 
 

@@ -193,6 +193,44 @@ def test_more_than_64_sequences(ctx, case, splits):
         ctx.set_option(mla.MLA_OPT_NUM_SPLITS, 0)
 
 
+# Lengths whose plain line starts sequences inside key ranges, so that the
+# plan follows every sequence with MLA_PLAN_SEQ_GAP line keys: short
+# sequences several to a range, long ones across many, more than 64 of them,
+# in every kernel mode.  (name, lens, s_q, H, page_size, key ranges)
+_rng = np.random.default_rng(31)
+GAPPED = [
+    ("70 mixed, one row block", [int(x) for x in np.concatenate([_rng.integers(20, 300, size=64),
+                                                                  _rng.integers(3000, 6000, size=6)])],
+     1, 16, 16, 64),
+    ("two key groups", [900, 33, 2500, 7, 1200], 2, 16, 0, 16),
+    ("one key group", [100, 2000, 50, 3000, 70, 900], 4, 16, 64, 32),
+    ("128 heads", [500, 4000, 90], 1, 128, 16, 8),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GAPPED)))
+def test_plan_with_sequence_gaps(ctx, case):
+    """The plan with gaps: the host mirror reports the gap, and host-sized
+    and blind launches (where every workgroup decides the gap itself) match
+    the oracle and each other bit for bit."""
+    import decode_attention_mla_amd as mla
+
+    name, lens, s_q, H, ps, splits = GAPPED[case]
+    announce(f"gapped plan: {name}, B={len(lens)} s_q={s_q} H={H} page={ps} ranges={splits}")
+    _, info = mla.mla_plan(lens, splits, 64)
+    assert info["seq_gap"] == 128, info
+    inp = wl.small("gap", len(lens), s_q, H, lens, page_size=ps, seed=900 + case)
+    ctx.set_option(mla.MLA_OPT_NUM_SPLITS, splits)
+    try:
+        o, l = run_gpu(ctx, inp)
+        ro, rl = oracle_of(inp)
+        compare(o, l, ro, rl, name)
+        o2, l2 = run_gpu(ctx, inp, host_lens=False)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2), f"{name}: blind launch differs"
+    finally:
+        ctx.set_option(mla.MLA_OPT_NUM_SPLITS, 0)
+
+
 def test_single_key_returns_value_row_exactly(ctx):
     announce("single key")
     inp = wl.small("one", 4, 1, 16, [1, 1, 1, 1], page_size=64, seed=5)

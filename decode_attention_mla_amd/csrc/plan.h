@@ -6,13 +6,12 @@
 // `chunk` keys.  When that line would start some sequence inside a range,
 // each sequence with keys is followed by kSeqGap line keys that hold no key,
 // and the ranges are cut from that line instead.  Workgroup g owns range
-// [g*chunk, (g+1)*chunk).  A range
-// meets a sequence in a segment.  A sequence inside one range is finished by
-// that workgroup; otherwise every segment writes a partial (normalized O and
-// log2-domain LSE) into slot 2*g + (segment does not start the range) and the
-// combine kernel merges the parts.  Each range holds at most one segment that
-// starts it and one that does not and is partial, so two slots per range
-// suffice.
+// [g*chunk, (g+1)*chunk).  A range meets a sequence in a segment.  A
+// sequence inside one range is finished by that workgroup; otherwise every
+// segment writes a partial (normalized O and log2-domain LSE) into slot
+// 2*g + (segment does not start the range) and the combine kernel merges the
+// parts.  Each range holds at most one segment that starts it and one that
+// does not and is partial, so two slots per range suffice.
 #pragma once
 
 #include <hip/hip_runtime.h>
